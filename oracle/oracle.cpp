@@ -1,0 +1,301 @@
+// oracle.cpp -- plain, slow CPU reference of one MoE decode layer with MXFP4
+// experts.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU
+// baseline leg of the benchmark call it; the library never does.  It shares
+// no code with the GPU library (no headers, helpers or tables) and reads only
+// the bytes the seeded generator writes.
+//
+// What is computed, and where it is stated
+//   * The layer: a router over E experts, top-k selection with renormalised
+//     softmax gates, one bf16 shared expert, k routed experts stored in MXFP4,
+//     each a SwiGLU gate/up/down chain, summed into the fp32 residual.  The
+//     per-layer work list (router, shared expert, 16 of 896 routed experts,
+//     MXFP4 experts of 17,547,264 bytes) is in "Kimi K3 on GB300: 13 kernels a
+//     layer, and what 842 and 423 tokens a second measure" (ai.thesatyajit.com),
+//     section "What one decode step of Kimi K3 does".
+//   * MXFP4: OCP Microscaling Formats (MX) v1.0 -- E2M1 elements (sign, 2-bit
+//     exponent with bias 1, 1-bit mantissa, no inf/NaN) and one E8M0 scale
+//     (2^(e-127), 0xFF = NaN) per block of 32 consecutive elements along K.
+//     Byte i of a row holds element 2i in bits 3:0 and element 2i+1 in 7:4.
+//
+// Precision: every dot product is accumulated in double in ascending index
+// order and rounded to fp32 once per stage value; elementwise steps are done
+// in double from the fp32 stage values and rounded to fp32.  The router logit
+// is the fp32 rounding of the double sum of bf16 x bf16 products (each exact
+// in double) plus the bias.  Top-k ranks the fp32 logits by (value
+// descending, index ascending); -0 and +0 compare equal.
+//
+// Parity pins for every function here live in tests/test_oracle_*.py.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+double bf16_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// fp32 -> bf16 with round-to-nearest-even, via an explicit significand
+// rounding in double (finite inputs).
+uint16_t float_to_bf16(float f) {
+  if (f == 0.0f || !std::isfinite(f)) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+  }
+  int e;
+  double m = std::frexp((double)f, &e);  // f = m * 2^e, 0.5 <= |m| < 1
+  // bf16 keeps 8 significant bits for normal numbers; below 2^-126 the
+  // quantum is fixed at 2^-133.
+  int keep = 8;
+  if (e - 1 < -126) keep = 8 - (-126 - (e - 1));
+  double q = std::nearbyint(std::ldexp(m, keep));  // default mode: ties to even
+  double r = std::ldexp(q, e - keep);
+  float rf = (float)r;  // exact: r has <= 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &rf, 4);
+  return (uint16_t)(u >> 16);
+}
+
+double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+uint64_t round256(uint64_t n) { return (n + 255) / 256 * 256; }
+
+struct Blob {
+  const uint8_t* codes[3];
+  const uint8_t* scales[3];
+};
+
+}  // namespace
+
+extern "C" {
+
+// ---- MXFP4 element and scale decode (OCP MX v1.0) -------------------------
+
+// E2M1: value = (-1)^s * (e == 0 ? m/2 : 2^(e-1) * (1 + m/2)).
+double oracle_e2m1(int code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -mag : mag;
+}
+
+// E8M0: 2^(byte - 127); byte 0xFF encodes NaN.
+double oracle_e8m0(int byte) {
+  if (byte == 0xFF) return std::nan("");
+  return std::ldexp(1.0, byte - 127);
+}
+
+// Byte size of one expert blob: gate codes [I][H/2], up codes [I][H/2],
+// down codes [H][I/2], gate scales [I][H/32], up scales [I][H/32],
+// down scales [H][I/32], each sub-array starting on a 256-byte boundary.
+uint64_t oracle_expert_bytes(int H, int I) {
+  uint64_t h = (uint64_t)H, i = (uint64_t)I;
+  return round256(i * h / 2) * 2 + round256(h * i / 2) + round256(i * h / 32) * 2 + round256(h * i / 32);
+}
+
+// w[n][k] = e2m1(code(n,k)) * e8m0(scale(n, k/32)) (exact in fp32 for the
+// scale bytes in use; NaN where the block scale is 0xFF).
+void oracle_decode_mxfp4(const uint8_t* codes, const uint8_t* scales, int N, int K, float* w) {
+  for (int n = 0; n < N; ++n)
+    for (int k = 0; k < K; ++k) {
+      uint8_t byte = codes[(size_t)n * (K / 2) + k / 2];
+      int code = (k & 1) ? (byte >> 4) : (byte & 15);
+      w[(size_t)n * K + k] = (float)(oracle_e2m1(code) * oracle_e8m0(scales[(size_t)n * (K / 32) + k / 32]));
+    }
+}
+
+static double mx_weight(const uint8_t* codes, const uint8_t* scales, int K, int n, int k) {
+  uint8_t byte = codes[(size_t)n * (K / 2) + k / 2];
+  int code = (k & 1) ? (byte >> 4) : (byte & 15);
+  return oracle_e2m1(code) * oracle_e8m0(scales[(size_t)n * (K / 32) + k / 32]);
+}
+
+// y[b][n] = fp32( sum_k w[n][k] * x[b][k] ), x bf16 (x_f32 == 0) or fp32.
+void oracle_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int N, int K, const void* x, int x_f32, int B,
+                       float* y) {
+  for (int b = 0; b < B; ++b)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) {
+        double xv = x_f32 ? (double)((const float*)x)[(size_t)b * K + k]
+                          : bf16_to_double(((const uint16_t*)x)[(size_t)b * K + k]);
+        acc += mx_weight(codes, scales, K, n, k) * xv;
+      }
+      y[(size_t)b * N + n] = (float)acc;
+    }
+}
+
+// ---- router -----------------------------------------------------------------
+
+// logits[b][e] = fp32( sum_h x[b][h] * Wr[e][h] + bias[e] ), summed in double.
+// Returns the number of logits whose ascending and descending double sums
+// differ (0 means the double sum did not depend on the order).
+int oracle_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int B, int H, int E,
+                         float* logits) {
+  int order_dependent = 0;
+  for (int b = 0; b < B; ++b)
+    for (int e = 0; e < E; ++e) {
+      double fwd = 0.0, rev = 0.0;
+      for (int h = 0; h < H; ++h)
+        fwd += bf16_to_double(x[(size_t)b * H + h]) * bf16_to_double(wr[(size_t)e * H + h]);
+      for (int h = H - 1; h >= 0; --h)
+        rev += bf16_to_double(x[(size_t)b * H + h]) * bf16_to_double(wr[(size_t)e * H + h]);
+      if (fwd != rev) ++order_dependent;
+      double l = fwd + (bias ? (double)bias[e] : 0.0);
+      logits[(size_t)b * E + e] = (float)l;
+    }
+  return order_dependent;
+}
+
+// Top-k by (logit descending, index ascending), then renormalised softmax over
+// the k selected: g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+void oracle_topk(const float* logits, int B, int E, int k, int32_t* idx, float* gate) {
+  std::vector<int> order(E);
+  for (int b = 0; b < B; ++b) {
+    const float* l = logits + (size_t)b * E;
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::sort(order.begin(), order.end(), [l](int a, int c) { return l[a] > l[c] || (l[a] == l[c] && a < c); });
+    double den = 0.0;
+    std::vector<double> num(k);
+    for (int j = 0; j < k; ++j) {
+      num[j] = std::exp((double)l[order[j]] - (double)l[order[0]]);
+      den += num[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      idx[(size_t)b * k + j] = order[j];
+      gate[(size_t)b * k + j] = (float)(num[j] / den);
+    }
+  }
+}
+
+// ---- SwiGLU experts ---------------------------------------------------------
+
+}  // extern "C"
+
+// One SwiGLU expert on one activation row, weights given as callables.
+template <class WG, class WU, class WD>
+static void swiglu_expert(int H, int I, const uint16_t* xrow, WG wg, WU wu, WD wd, float* o) {
+  std::vector<float> h(I);
+  for (int n = 0; n < I; ++n) {
+    double g = 0.0, u = 0.0;
+    for (int k = 0; k < H; ++k) {
+      double xv = bf16_to_double(xrow[k]);
+      g += wg(n, k) * xv;
+      u += wu(n, k) * xv;
+    }
+    float gf = (float)g, uf = (float)u;
+    h[n] = (float)(silu((double)gf) * (double)uf);
+  }
+  for (int m = 0; m < H; ++m) {
+    double acc = 0.0;
+    for (int n = 0; n < I; ++n) acc += wd(m, n) * (double)h[n];
+    o[m] = (float)acc;
+  }
+}
+
+extern "C" {
+
+// Shared expert (bf16 weights gate/up [Is][H], down [H][Is]) on x[b].
+void oracle_shared_expert(const uint16_t* wg, const uint16_t* wu, const uint16_t* wd, int H, int Is,
+                          const uint16_t* x, int B, float* out) {
+  for (int b = 0; b < B; ++b)
+    swiglu_expert(
+        H, Is, x + (size_t)b * H, [&](int n, int k) { return bf16_to_double(wg[(size_t)n * H + k]); },
+        [&](int n, int k) { return bf16_to_double(wu[(size_t)n * H + k]); },
+        [&](int m, int n) { return bf16_to_double(wd[(size_t)m * Is + n]); }, out + (size_t)b * H);
+}
+
+static Blob blob_view(const uint8_t* base, int H, int I) {
+  uint64_t h = (uint64_t)H, i = (uint64_t)I;
+  uint64_t o0 = 0, o1 = o0 + round256(i * h / 2), o2 = o1 + round256(i * h / 2), o3 = o2 + round256(h * i / 2),
+           o4 = o3 + round256(i * h / 32), o5 = o4 + round256(i * h / 32);
+  Blob bl;
+  bl.codes[0] = base + o0;
+  bl.codes[1] = base + o1;
+  bl.codes[2] = base + o2;
+  bl.scales[0] = base + o3;
+  bl.scales[1] = base + o4;
+  bl.scales[2] = base + o5;
+  return bl;
+}
+
+// One routed MXFP4 expert (blob layout of oracle_expert_bytes) on x[b].
+void oracle_routed_expert(const uint8_t* blob, int H, int I, const uint16_t* x, int B, float* out) {
+  Blob bl = blob_view(blob, H, I);
+  for (int b = 0; b < B; ++b)
+    swiglu_expert(
+        H, I, x + (size_t)b * H, [&](int n, int k) { return mx_weight(bl.codes[0], bl.scales[0], H, n, k); },
+        [&](int n, int k) { return mx_weight(bl.codes[1], bl.scales[1], H, n, k); },
+        [&](int m, int n) { return mx_weight(bl.codes[2], bl.scales[2], I, m, n); }, out + (size_t)b * H);
+}
+
+// ---- whole layer --------------------------------------------------------------
+
+// out[b] = fp32( residual[b] + shared(x[b]) + sum_j gate[b][j] * expert_{idx[b][j]}(x[b]) ),
+// the sum over j taken in ascending j, all in double.
+// experts[e] points at expert e's blob; entries for experts no row selects
+// may be NULL.  Optional outputs: logits [B][E], shared_out [B][H],
+// slot_out [B][k][H].  Returns -1 if a selected expert has no blob, else the
+// router's order-dependence count.
+int oracle_moe_layer(int H, int I, int E, int k, int Is, const uint16_t* router_w, const float* router_bias,
+                     const uint16_t* shared_gate, const uint16_t* shared_up, const uint16_t* shared_down,
+                     const uint8_t* const* experts, const uint16_t* x, const float* residual, int B, float* out,
+                     int32_t* idx, float* gate, float* logits_out, float* shared_out, float* slot_out) {
+  std::vector<float> logits((size_t)B * E);
+  int od = oracle_router_logits(x, router_w, router_bias, B, H, E, logits.data());
+  oracle_topk(logits.data(), B, E, k, idx, gate);
+  if (logits_out) std::memcpy(logits_out, logits.data(), sizeof(float) * logits.size());
+  std::vector<float> os((size_t)H, 0.0f), oj((size_t)k * H);
+  for (int b = 0; b < B; ++b) {
+    const uint16_t* xb = x + (size_t)b * H;
+    if (Is > 0) oracle_shared_expert(shared_gate, shared_up, shared_down, H, Is, xb, 1, os.data());
+    for (int j = 0; j < k; ++j) {
+      const uint8_t* blob = experts[idx[(size_t)b * k + j]];
+      if (!blob) return -1;
+      oracle_routed_expert(blob, H, I, xb, 1, oj.data() + (size_t)j * H);
+    }
+    for (int m = 0; m < H; ++m) {
+      double acc = (double)residual[(size_t)b * H + m] + (double)os[m];
+      for (int j = 0; j < k; ++j) acc += (double)gate[(size_t)b * k + j] * (double)oj[(size_t)j * H + m];
+      out[(size_t)b * H + m] = (float)acc;
+    }
+    if (shared_out) std::memcpy(shared_out + (size_t)b * H, os.data(), sizeof(float) * H);
+    if (slot_out) std::memcpy(slot_out + (size_t)b * k * H, oj.data(), sizeof(float) * (size_t)k * H);
+  }
+  return od;
+}
+
+// ---- dense block pieces of the layer stack ----------------------------------
+
+// bf16 rounding (round to nearest even) of fp32 values, exposed for the pins.
+void oracle_to_bf16(const float* in, uint64_t n, uint16_t* out) {
+  for (uint64_t i = 0; i < n; ++i) out[i] = float_to_bf16(in[i]);
+}
+
+// out[b] = bf16( fp32( h[b] / sqrt(mean(h[b]^2) + eps) ) ), gain 1.
+void oracle_rmsnorm_bf16(const float* h, int B, int H, double eps, uint16_t* out) {
+  for (int b = 0; b < B; ++b) {
+    double ss = 0.0;
+    for (int i = 0; i < H; ++i) ss += (double)h[(size_t)b * H + i] * (double)h[(size_t)b * H + i];
+    double r = 1.0 / std::sqrt(ss / H + eps);
+    for (int i = 0; i < H; ++i) out[(size_t)b * H + i] = float_to_bf16((float)((double)h[(size_t)b * H + i] * r));
+  }
+}
+
+// y[b][n] = bf16( fp32( sum_k W[n][k] * x[b][k] ) ), W bf16 [N][K], x bf16 [B][K].
+void oracle_dense_gemv_bf16(const uint16_t* w, int N, int K, const uint16_t* x, int B, uint16_t* y) {
+  for (int b = 0; b < B; ++b)
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) acc += bf16_to_double(w[(size_t)n * K + k]) * bf16_to_double(x[(size_t)b * K + k]);
+      y[(size_t)b * N + n] = float_to_bf16((float)acc);
+    }
+}
+
+}  // extern "C"
