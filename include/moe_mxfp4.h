@@ -1,0 +1,178 @@
+/*
+ * moe_mxfp4.h -- C ABI of the MI355X (gfx950) MXFP4 mixture-of-experts
+ * decode-layer library (libmoe_mxfp4.so).
+ *
+ * The operation.  One decode step of one mixture-of-experts layer of the kind
+ * described in "Kimi K3 on GB300: 13 kernels a layer, and what 842 and 423
+ * tokens a second measure" (ai.thesatyajit.com), section "What one decode
+ * step of Kimi K3 does": per token a router scores 896 experts, 16 are routed
+ * to, a shared expert runs beside them, and the experts are stored in MXFP4
+ * (17,547,264 bytes each at hidden 7168, expert intermediate 1536).  For each
+ * activation row b of a batch of 1..64 (the decode envelope of "vLLM reports
+ * 842 tokens per second for Kimi decoding with NVIDIA DSpark", ai-primer.com,
+ * list of the supported envelope):
+ *
+ *   logit[e] = fp32( sum_h x[b][h] * Wr[e][h] + bias[e] )
+ *   S        = the top_k experts by (logit descending, index ascending)
+ *   gate[j]  = exp(logit[S_j] - logit[S_0]) / sum_i exp(logit[S_i] - logit[S_0])
+ *   FFN_W(x) = W_down ( silu(W_gate x) * (W_up x) ),   silu(z) = z / (1 + e^-z)
+ *   residual[b] += FFN_shared(x[b]) + sum_j gate[j] * FFN_{S_j}(x[b])
+ *
+ * MXFP4 (OCP Microscaling Formats v1.0): each weight is a 4-bit E2M1 code
+ * (sign, 2-bit exponent with bias 1, 1-bit mantissa: magnitudes 0, .5, 1,
+ * 1.5, 2, 3, 4, 6), and each block of 32 consecutive elements along the
+ * contraction dimension K of one output row shares an E8M0 scale byte
+ * (2^(byte-127); 0xFF is NaN).  Codes are packed two per byte, element 2i in
+ * bits 3:0 and element 2i+1 in bits 7:4.  A matrix [N][K] is stored as codes
+ * [N][K/2] bytes and scales [N][K/32] bytes, both row-major.
+ *
+ * Expert blob.  Routed expert e occupies moe_expert_bytes(H, I) bytes at
+ * experts + e * moe_expert_bytes(H, I), holding, each sub-array starting at a
+ * multiple of 256 bytes (no padding occurs at H 7168, I 1536):
+ *     gate codes [I][H/2] | up codes [I][H/2] | down codes [H][I/2] |
+ *     gate scales [I][H/32] | up scales [I][H/32] | down scales [H][I/32]
+ *
+ * Precision.  Router products bf16 x bf16 are exact; they are summed in fp64
+ * and rounded once to fp32 (so expert selection is reproducible bit for bit).
+ * Expert and shared-expert dot products are accumulated in fp32; the SwiGLU
+ * intermediate is kept in fp32; the combine is fp32.
+ *
+ * Conventions for every entry point.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises, and keeps no state
+ *     between calls.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and runs asynchronously; results are visible after the
+ *     caller synchronises that stream.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and return MOE_ERR_INVALID_ARGUMENT; shapes outside the kernels'
+ *     envelope return MOE_ERR_UNSUPPORTED (the caller runs something else);
+ *     a failed launch returns MOE_ERR_HIP.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Buffers must not alias unless stated.  Device pointers must be aligned
+ *     to 16 bytes (bf16/fp32 tensors) and 256 bytes (expert blobs, workspace).
+ *   - Concurrent calls are safe when they use distinct workspaces and
+ *     outputs.  Non-finite inputs are not checked; a 0xFF scale byte makes
+ *     NaN every output that depends on its block.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = -1,    /* NULL pointer, bad size, bad alignment   */
+  MOE_ERR_UNSUPPORTED = -2,         /* valid, but beyond the kernels' envelope */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -3, /* ws_bytes < moe_workspace_size(...)      */
+  MOE_ERR_HIP = -4                  /* a HIP runtime call or launch failed     */
+} moe_status;
+
+typedef enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 } moe_dtype;
+
+/* Largest batch (activation rows) any entry point accepts. */
+#define MOE_MAX_BATCH 64
+/* Largest top_k and number of experts the router/top-k kernels accept. */
+#define MOE_MAX_TOPK 64
+#define MOE_MAX_EXPERTS 4096
+
+/*
+ * One layer's weights: a host struct of device pointers.
+ *   hidden H, inter I (routed expert intermediate), num_experts E, top_k k,
+ *   shared_inter Is (0 = no shared expert).  H and I multiples of 32,
+ *   Is a multiple of 8.
+ *   router_w     bf16 [E][H] (row e scores expert e)
+ *   router_bias  fp32 [E], added to the logits before selection and gates;
+ *                NULL for none
+ *   shared_gate, shared_up  bf16 [Is][H];  shared_down  bf16 [H][Is];
+ *                all three NULL iff Is == 0
+ *   experts      E blobs of moe_expert_bytes(H, I) bytes (layout above)
+ * bf16 tensors are raw bfloat16 bit patterns (uint16_t).
+ */
+typedef struct {
+  int32_t hidden, inter, num_experts, top_k, shared_inter;
+  const uint16_t* router_w;
+  const float* router_bias;
+  const uint16_t* shared_gate;
+  const uint16_t* shared_up;
+  const uint16_t* shared_down;
+  const uint8_t* experts;
+} moe_layer_weights;
+
+/* Bytes of one expert blob (17,547,264 at H 7168, I 1536); 0 if H or I is
+ * not a positive multiple of 32. */
+size_t moe_expert_bytes(int hidden, int inter);
+
+/* Workspace bytes moe_decode_layer needs for this layer at this batch.
+ * Returns MOE_ERR_INVALID_ARGUMENT for the same shape errors as
+ * moe_decode_layer. */
+moe_status moe_workspace_size(const moe_layer_weights* w, int batch, size_t* bytes);
+
+/*
+ * router_topk -- router GEMV, top-k selection and renormalised gates.
+ *   x          bf16 [batch][hidden]
+ *   router_w   bf16 [num_experts][hidden]; bias fp32 [num_experts] or NULL
+ *   topk_idx   out int32 [batch][top_k], experts in (logit desc, index asc)
+ *              order -- ties resolve to the lower index
+ *   topk_gate  out fp32 [batch][top_k], gates in the same order, sum 1
+ *   logits     out fp32 [batch][num_experts] (the router scores), or NULL
+ *   ws         device workspace of >= moe_router_workspace_size(...) bytes
+ *              (may be NULL when that size is 0)
+ * 1 <= batch <= 64, 1 <= top_k <= min(num_experts, 64),
+ * num_experts <= 4096, hidden a multiple of 32 and <= 16384.
+ */
+size_t moe_router_workspace_size(int batch, int num_experts);
+moe_status router_topk(const uint16_t* x, int batch, int hidden, const uint16_t* router_w, const float* bias,
+                       int num_experts, int top_k, int32_t* topk_idx, float* topk_gate, float* logits, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * expert_gemv_mxfp4 -- y[b][n] = sum_k dequant(W)[n][k] * x[b][k], fp32.
+ *   codes   [n][k/2] bytes, scales [n][k/32] bytes (one MXFP4 matrix)
+ *   x       [batch][k], bf16 (x_dtype MOE_DTYPE_BF16) or fp32
+ *   y       out fp32 [batch][n]; must not alias x
+ * k a multiple of 32 (<= 16384), 1 <= n, 1 <= batch <= 64.
+ */
+moe_status expert_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int n, int k, const void* x,
+                             moe_dtype x_dtype, int batch, float* y, void* stream);
+
+/*
+ * moe_decode_layer -- the whole layer for `batch` rows.
+ *   x          bf16 [batch][hidden], the layer input (normalised activations)
+ *   residual   fp32 [batch][hidden], read and overwritten with
+ *              residual + shared + sum_j gate_j * expert_j; must not alias x
+ *   topk_idx   out int32 [batch][top_k]; topk_gate out fp32 [batch][top_k]
+ *   ws         workspace of >= moe_workspace_size(w, batch) bytes, 256-byte
+ *              aligned, owned by the caller; its contents on entry are
+ *              ignored (the library clears what it needs)
+ * Routing never leaves the device: no host synchronisation happens inside.
+ */
+moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                            int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense-block pieces used between MoE layers of a decode-step stack.
+ * rmsnorm_bf16:    out[b] = bf16( in[b] / sqrt(mean(in[b]^2) + eps) ), gain 1;
+ *                  in fp32 [batch][hidden], out bf16 [batch][hidden].
+ * dense_gemv_bf16: y[b][n] = bf16( sum_k W[n][k] * x[b][k] ) with fp32
+ *                  accumulation; W bf16 [n][k], x bf16 [batch][k], y bf16
+ *                  [batch][n]; y must not alias x.  k a multiple of 8.
+ * residual_add_bf16: h[b][i] += float(t[b][i]) (h fp32, t bf16).
+ */
+moe_status rmsnorm_bf16(const float* in, int batch, int hidden, float eps, uint16_t* out, void* stream);
+moe_status dense_gemv_bf16(const uint16_t* w, int n, int k, const uint16_t* x, int batch, uint16_t* y,
+                           void* stream);
+moe_status residual_add_bf16(float* h, const uint16_t* t, int batch, int hidden, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,194 @@
+"""Python binding of libmoe_mxfp4.so, the MI355X MXFP4 MoE decode-layer library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (bf16 data may be
+torch.bfloat16 or int16/uint16 bit patterns); work goes on the current torch
+stream unless a stream is given.  If the library is not built, loading
+raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
+MAX_BATCH = 64
+
+# Symbols the C header declares (checked by tests/test_abi.py).
+EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size", "router_topk",
+           "expert_gemv_mxfp4", "moe_decode_layer", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16",
+           "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class LayerWeightsC(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("shared_gate", ctypes.c_void_p), ("shared_up", ctypes.c_void_p),
+                ("shared_down", ctypes.c_void_p), ("experts", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Load the built library (raises if it is missing: no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run memory_bound_mxfp4_amd.build.build() "
+                          "or __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "moe_expert_bytes": (Z, [I, I]),
+        "moe_workspace_size": (I, [P, I, ctypes.POINTER(Z)]),
+        "moe_router_workspace_size": (Z, [I, I]),
+        "router_topk": (I, [P, I, I, P, P, I, I, P, P, P, P, Z, P]),
+        "expert_gemv_mxfp4": (I, [P, P, I, I, P, I, I, P, P]),
+        "moe_decode_layer": (I, [P, P, P, I, P, P, P, Z, P]),
+        "rmsnorm_bf16": (I, [P, I, I, F, P, P]),
+        "dense_gemv_bf16": (I, [P, I, I, P, I, P, P]),
+        "residual_add_bf16": (I, [P, P, I, I, P]),
+        "moe_status_string": (ctypes.c_char_p, [I]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(status).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != MOE_OK:
+        raise MoeError(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def expert_bytes(hidden: int, inter: int) -> int:
+    return int(load().moe_expert_bytes(hidden, inter))
+
+
+@dataclass
+class LayerWeights:
+    """One layer's weights (device tensors) and shape."""
+    hidden: int
+    inter: int
+    num_experts: int
+    top_k: int
+    shared_inter: int
+    router_w: object
+    experts: object
+    router_bias: Optional[object] = None
+    shared_gate: Optional[object] = None
+    shared_up: Optional[object] = None
+    shared_down: Optional[object] = None
+
+    def c_struct(self) -> LayerWeightsC:
+        return LayerWeightsC(self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter,
+                             _ptr(self.router_w), _ptr(self.router_bias), _ptr(self.shared_gate),
+                             _ptr(self.shared_up), _ptr(self.shared_down), _ptr(self.experts))
+
+
+def workspace_size(w: LayerWeights, batch: int) -> int:
+    n = ctypes.c_size_t(0)
+    cs = w.c_struct()
+    _check(load().moe_workspace_size(ctypes.byref(cs), batch, ctypes.byref(n)), "moe_workspace_size")
+    return int(n.value)
+
+
+def alloc_workspace(w: LayerWeights, batch: int, device=None):
+    import torch
+    return torch.empty(workspace_size(w, batch), dtype=torch.uint8, device=device or w.router_w.device)
+
+
+def router_topk(x, router_w, top_k: int, bias=None, idx=None, gate=None, logits=None, ws=None, stream=None):
+    """Router GEMV + top-k + renormalised gates. Returns (idx int32 [B][k], gate fp32 [B][k])."""
+    import torch
+    B, H = x.shape
+    E = router_w.shape[0]
+    dev = x.device
+    idx = torch.empty((B, top_k), dtype=torch.int32, device=dev) if idx is None else idx
+    gate = torch.empty((B, top_k), dtype=torch.float32, device=dev) if gate is None else gate
+    if logits is None and ws is None:
+        ws = torch.empty(load().moe_router_workspace_size(B, E), dtype=torch.uint8, device=dev)
+    _check(load().router_topk(_ptr(x), B, H, _ptr(router_w), _ptr(bias), E, top_k, _ptr(idx), _ptr(gate),
+                              _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "router_topk")
+    return idx, gate
+
+
+def expert_gemv_mxfp4(codes, scales, x, n: int, k: int, y=None, stream=None):
+    """y[b][n] = dequant(codes, scales) . x[b]; x bf16 or fp32 [B][k]. Returns y fp32 [B][n]."""
+    import torch
+    B = x.shape[0]
+    y = torch.empty((B, n), dtype=torch.float32, device=x.device) if y is None else y
+    xdt = MOE_DTYPE_F32 if x.dtype == torch.float32 else MOE_DTYPE_BF16
+    _check(load().expert_gemv_mxfp4(_ptr(codes), _ptr(scales), n, k, _ptr(x), xdt, B, _ptr(y), _stream(stream)),
+           "expert_gemv_mxfp4")
+    return y
+
+
+def moe_decode_layer(w: LayerWeights, x, residual, idx=None, gate=None, ws=None, stream=None):
+    """The whole layer; `residual` (fp32 [B][H]) is updated in place. Returns (idx, gate)."""
+    import torch
+    B = x.shape[0]
+    dev = x.device
+    idx = torch.empty((B, w.top_k), dtype=torch.int32, device=dev) if idx is None else idx
+    gate = torch.empty((B, w.top_k), dtype=torch.float32, device=dev) if gate is None else gate
+    ws = alloc_workspace(w, B, dev) if ws is None else ws
+    cs = w.c_struct()
+    _check(load().moe_decode_layer(ctypes.byref(cs), _ptr(x), _ptr(residual), B, _ptr(idx), _ptr(gate), _ptr(ws),
+                                   ws.numel(), _stream(stream)), "moe_decode_layer")
+    return idx, gate
+
+
+def rmsnorm_bf16(h, eps: float = 1e-6, out=None, stream=None):
+    import torch
+    B, H = h.shape
+    out = torch.empty((B, H), dtype=torch.bfloat16, device=h.device) if out is None else out
+    _check(load().rmsnorm_bf16(_ptr(h), B, H, float(eps), _ptr(out), _stream(stream)), "rmsnorm_bf16")
+    return out
+
+
+def dense_gemv_bf16(w, x, y=None, stream=None):
+    import torch
+    n, k = w.shape
+    B = x.shape[0]
+    y = torch.empty((B, n), dtype=torch.bfloat16, device=x.device) if y is None else y
+    _check(load().dense_gemv_bf16(_ptr(w), n, k, _ptr(x), B, _ptr(y), _stream(stream)), "dense_gemv_bf16")
+    return y
+
+
+def residual_add_bf16(h, t, stream=None):
+    B, H = h.shape
+    _check(load().residual_add_bf16(_ptr(h), _ptr(t), B, H, _stream(stream)), "residual_add_bf16")
+    return h

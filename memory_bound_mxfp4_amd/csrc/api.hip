@@ -1,0 +1,207 @@
+// api.hip -- the C ABI of libmoe_mxfp4.so: argument validation, workspace
+// layout and kernel launches.  Semantics are documented in moe_mxfp4.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "internal.h"
+#include "moe_mxfp4.h"
+
+namespace moe {
+
+BlobLayout blob_layout(int H, int I) {
+  size_t h = (size_t)H, i = (size_t)I;
+  size_t sz[6] = {i * h / 2, i * h / 2, h * i / 2, i * h / 32, i * h / 32, h * i / 32};
+  BlobLayout L;
+  size_t o = 0;
+  for (int m = 0; m < 6; ++m) {
+    L.off[m] = o;
+    o += align256(sz[m]);
+  }
+  L.bytes = o;
+  return L;
+}
+
+Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B) {
+  char* p = static_cast<char*>(base);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + o : nullptr;
+    o += align256(bytes);
+    return r;
+  };
+  Workspace w;
+  const size_t slots = (size_t)B * k;
+  const size_t umax = slots < (size_t)E ? slots : (size_t)E;
+  w.logits = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * E));
+  w.sched.n_active = reinterpret_cast<int*>(take(sizeof(int)));
+  w.sched.active = reinterpret_cast<int*>(take(sizeof(int) * umax));
+  w.sched.row_off = reinterpret_cast<int*>(take(sizeof(int) * (umax + 1)));
+  w.sched.rows = reinterpret_cast<int*>(take(sizeof(int) * slots));
+  w.h_shared = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * (Is > 0 ? Is : 1)));
+  w.h_routed = reinterpret_cast<float*>(take(sizeof(float) * slots * I));
+  w.o_shared = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * H));
+  w.o_routed = reinterpret_cast<float*>(take(sizeof(float) * slots * H));
+  w.bytes = o;
+  return w;
+}
+
+int num_cus() {
+  static std::atomic<int> cached{0};
+  int v = cached.load();
+  if (v > 0) return v;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cached.store(n);
+  return n;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+static inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static moe_status check_layer(const moe_layer_weights* w, int batch) {
+  if (!w) return MOE_ERR_INVALID_ARGUMENT;
+  const int H = w->hidden, I = w->inter, E = w->num_experts, k = w->top_k, Is = w->shared_inter;
+  if (H <= 0 || I <= 0 || E <= 0 || k <= 0 || Is < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (H % 32 || I % 32 || Is % 8) return MOE_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || batch > MOE_MAX_BATCH) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > E || k > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARGUMENT;
+  if (!w->router_w || !w->experts) return MOE_ERR_INVALID_ARGUMENT;
+  if (Is > 0 && (!w->shared_gate || !w->shared_up || !w->shared_down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (Is == 0 && (w->shared_gate || w->shared_up || w->shared_down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(w->router_w, 16) || !aligned(w->experts, 256) || (w->router_bias && !aligned(w->router_bias, 4)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (Is > 0 && (!aligned(w->shared_gate, 16) || !aligned(w->shared_up, 16) || !aligned(w->shared_down, 16)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  // kernel envelope: activation rows staged in 64 KB of LDS, keys per lane
+  if (H > 16384 || I > 16384 || Is > 16384 || E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+extern "C" {
+
+size_t moe_expert_bytes(int hidden, int inter) {
+  if (hidden <= 0 || inter <= 0 || hidden % 32 || inter % 32) return 0;
+  return blob_layout(hidden, inter).bytes;
+}
+
+moe_status moe_workspace_size(const moe_layer_weights* w, int batch, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_layer(w, batch);
+  if (st != MOE_OK) return st;
+  *bytes = ws_layout(nullptr, w->hidden, w->inter, w->num_experts, w->top_k, w->shared_inter, batch).bytes;
+  return MOE_OK;
+}
+
+size_t moe_router_workspace_size(int batch, int num_experts) {
+  if (batch < 1 || num_experts < 1) return 0;
+  return align256(sizeof(float) * (size_t)batch * num_experts);
+}
+
+moe_status router_topk(const uint16_t* x, int batch, int hidden, const uint16_t* router_w, const float* bias,
+                       int num_experts, int top_k, int32_t* topk_idx, float* topk_gate, float* logits, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!x || !router_w || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || batch > MOE_MAX_BATCH || hidden <= 0 || hidden % 32 || num_experts < 1 || top_k < 1 ||
+      top_k > num_experts || top_k > MOE_MAX_TOPK)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(router_w, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (hidden > 16384 || num_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  float* lg = logits;
+  if (!lg) {
+    if (!ws) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < moe_router_workspace_size(batch, num_experts)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    lg = static_cast<float*>(ws);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_router_logits(x, batch, hidden, router_w, bias, num_experts, lg, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_topk(lg, batch, num_experts, top_k, topk_idx, topk_gate, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status expert_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int n, int k, const void* x,
+                             moe_dtype x_dtype, int batch, float* y, void* stream) {
+  if (!codes || !scales || !x || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (n < 1 || k < 32 || k % 32 || batch < 1 || batch > MOE_MAX_BATCH) return MOE_ERR_INVALID_ARGUMENT;
+  if (x_dtype != MOE_DTYPE_BF16 && x_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > 16384) return MOE_ERR_UNSUPPORTED;
+  if (launch_gemv_mxfp4(codes, scales, n, k, x, x_dtype == MOE_DTYPE_F32, batch, y, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                            int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_layer(w, batch);
+  if (st != MOE_OK) return st;
+  if (!x || !residual || !topk_idx || !topk_gate || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(ws, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  const int H = w->hidden, I = w->inter, E = w->num_experts, k = w->top_k, Is = w->shared_inter;
+  Workspace wsl = ws_layout(ws, H, I, E, k, Is, batch);
+  if (ws_bytes < wsl.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_router_logits(x, batch, H, w->router_w, w->router_bias, E, wsl.logits, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_topk(wsl.logits, batch, E, k, topk_idx, topk_gate, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_schedule(topk_idx, batch, k, E, wsl.sched, s) != hipSuccess) return MOE_ERR_HIP;
+  LayerArgs a;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.k = k;
+  a.Is = Is;
+  a.B = batch;
+  a.x = x;
+  a.sg = w->shared_gate;
+  a.su = w->shared_up;
+  a.sd = w->shared_down;
+  a.experts = w->experts;
+  a.blob = blob_layout(H, I);
+  a.gate = topk_gate;
+  a.ws = wsl;
+  a.residual = residual;
+  if (launch_experts(a, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status rmsnorm_bf16(const float* in, int batch, int hidden, float eps, uint16_t* out, void* stream) {
+  if (!in || !out || batch < 1 || batch > MOE_MAX_BATCH || hidden < 1 || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (launch_rmsnorm(in, batch, hidden, eps, out, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status dense_gemv_bf16(const uint16_t* w, int n, int k, const uint16_t* x, int batch, uint16_t* y,
+                           void* stream) {
+  if (!w || !x || !y || n < 1 || k < 8 || k % 8 || batch < 1 || batch > MOE_MAX_BATCH) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(w, 16) || !aligned(x, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > 32768) return MOE_ERR_UNSUPPORTED;
+  if (launch_dense_gemv(w, n, k, x, batch, y, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status residual_add_bf16(float* h, const uint16_t* t, int batch, int hidden, void* stream) {
+  if (!h || !t || batch < 1 || batch > MOE_MAX_BATCH || hidden < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (launch_residual_add(h, t, batch, hidden, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// dense.hip -- the bf16 dense block between MoE layers of a decode-step
+// stack: RMSNorm (gain 1) to bf16, a bf16 GEMV with fp32 accumulation rounded
+// to bf16, and the residual add.  The dense bf16 trunk that every token reads
+// is described in "Kimi K3 on GB300: 13 kernels a layer" (section "What one
+// decode step of Kimi K3 does"); like the experts it is one row against a
+// weight matrix, so the GEMV streams each weight byte once with 16-byte
+// non-temporal loads.
+#include "internal.h"
+#include "mx_common.h"
+
+namespace moe {
+
+// out[b] = bf16( in[b] * rsqrt(mean(in[b]^2) + eps) ).  grid: B blocks x 256.
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ in, int H, float eps,
+                                                 uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int b = blockIdx.x;
+  const float* row = in + (size_t)b * H;
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < H; i += 256) ss = fmaf(row[i], row[i], ss);
+  ss = sum_lanes<64>(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += 256) out[(size_t)b * H + i] = f32_to_bf16(row[i] * r);
+}
+
+hipError_t launch_rmsnorm(const float* in, int B, int H, float eps, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(256), 0, s, in, H, eps, out);
+  return hipGetLastError();
+}
+
+// y[b][n] = bf16( sum_k W[n][k] x[b][k] ).  Half a wave per weight row (two
+// rows per wave, eight per block); x rows staged in LDS RG at a time.
+template <int RG>
+__global__ __launch_bounds__(256) void k_dense_gemv(const uint16_t* __restrict__ w, int N, int K,
+                                                    const uint16_t* __restrict__ x, int B, uint16_t* __restrict__ y) {
+  extern __shared__ u32x4 lds_raw[];
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(lds_raw);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int n = blockIdx.x * 8 + wave * 2 + half;
+  const int C8 = K / 8;
+  for (int g0 = 0; g0 < B; g0 += RG) {
+    const int nr = min(RG, B - g0);
+    __syncthreads();
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)g0 * K);
+    for (int i = threadIdx.x; i < nr * C8; i += 256) lds_raw[i] = src[i];
+    __syncthreads();
+    float acc[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = 0.0f;
+    if (n < N) {
+      const uint16_t* wr = w + (size_t)n * K;
+      for (int c0 = l32; c0 < C8; c0 += 32 * 8) {
+        u32x4 q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          int c = c0 + 32 * i;
+          if (c < C8) q[i] = ld_weight16(wr + 8 * (size_t)c);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          int c = c0 + 32 * i;
+          if (c < C8) {
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+              if (r < nr) {
+                u32x4 xv = reinterpret_cast<const u32x4*>(xs + (size_t)r * K)[c];
+                float a = acc[r];
+                a = dot2_bf16(q[i][0], xv[0], a);
+                a = dot2_bf16(q[i][1], xv[1], a);
+                a = dot2_bf16(q[i][2], xv[2], a);
+                a = dot2_bf16(q[i][3], xv[3], a);
+                acc[r] = a;
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      if (r < nr) {
+        float v = sum_lanes<32>(acc[r]);
+        if (l32 == 0 && n < N) y[(size_t)(g0 + r) * N + n] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+hipError_t launch_dense_gemv(const uint16_t* w, int N, int K, const uint16_t* x, int B, uint16_t* y, hipStream_t s) {
+  size_t row_bytes = (size_t)K * 2;
+  int rg = B <= 1 ? 1 : (B <= 2 ? 2 : 4);
+  while (rg > 1 && rg * row_bytes > 65536) rg >>= 1;
+  size_t lds = rg * row_bytes;
+  dim3 grid((N + 7) / 8), block(256);
+  if (rg == 1) hipLaunchKernelGGL(k_dense_gemv<1>, grid, block, lds, s, w, N, K, x, B, y);
+  else if (rg == 2) hipLaunchKernelGGL(k_dense_gemv<2>, grid, block, lds, s, w, N, K, x, B, y);
+  else hipLaunchKernelGGL(k_dense_gemv<4>, grid, block, lds, s, w, N, K, x, B, y);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_residual_add(float* __restrict__ h, const uint16_t* __restrict__ t, size_t n) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) h[i] += __uint_as_float((uint32_t)t[i] << 16);
+}
+
+hipError_t launch_residual_add(float* h, const uint16_t* t, int B, int H, hipStream_t s) {
+  size_t n = (size_t)B * H;
+  hipLaunchKernelGGL(k_residual_add, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, t, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

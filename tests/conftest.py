@@ -28,3 +28,16 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def k3_layer():
+    """The K3-shaped layer (seed 0) in HBM, shared by the GPU tests of a session."""
+    import torch
+    from layer_inputs import device_weights
+    from synth import CONFIGS
+    print("[fixture] generating the K3-shaped layer (seed 0) on the device", flush=True)
+    w = device_weights(CONFIGS["k3_b1"], 0)
+    yield w
+    del w
+    torch.cuda.empty_cache()

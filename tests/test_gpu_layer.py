@@ -1,0 +1,150 @@
+"""GPU parity of moe_decode_layer against the oracle on the tiny layer and the
+K3-shaped layer at batch 1, 8 and 64 (Zipf-biased router): expert indices
+bit-exact, outputs within 2e-3 relative L2 per row."""
+import numpy as np
+import pytest
+
+import memory_bound_mxfp4_amd as moe
+import oracle
+import synth
+from layer_inputs import (device_weights, host_experts, host_weights, oracle_layer, rel_l2_rows, residual_from_x,
+                          x_host)
+from synth import CONFIGS
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _run_layer(w, x, res):
+    import torch
+    r = _dev(res.copy())
+    idx, gate = moe.moe_decode_layer(w, _dev(x), r)
+    torch.cuda.synchronize()
+    return r.cpu().numpy(), idx.cpu().numpy(), gate.cpu().numpy()
+
+
+def _check(cfg, seed, x, res, out, idx, gate, rows=None):
+    rows = list(range(x.shape[0])) if rows is None else rows
+    ref = oracle_layer(cfg, seed, x[rows], res[rows])
+    assert np.array_equal(idx[rows], ref["idx"])
+    assert np.abs(gate[rows] - ref["gate"]).max() <= 1e-6
+    err = rel_l2_rows(out[rows], ref["out"])
+    delta = rel_l2_rows(out[rows] - res[rows], ref["out"] - res[rows])
+    print(f"    max rel-L2 out {err.max():.3e}  moe-delta {delta.max():.3e}", flush=True)
+    assert err.max() <= TOL
+    assert delta.max() <= TOL
+    return ref
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_tiny_layer(seed):
+    cfg = CONFIGS["tiny"]
+    print(f"[case] layer tiny seed {seed}", flush=True)
+    w = device_weights(cfg, seed)
+    x = x_host(cfg, seed)
+    res = residual_from_x(x)
+    out, idx, gate = _run_layer(w, x, res)
+    _check(cfg, seed, x, res, out, idx, gate)
+
+
+def test_tiny_layer_batches_and_top_k_equal_e():
+    cfg = CONFIGS["tiny"]
+    print("[case] layer tiny B=1..64 and k=E", flush=True)
+    w = device_weights(cfg, 7)
+    for B in (2, 5, 64):
+        x = x_host(cfg, 7, batch=B)
+        res = residual_from_x(x)
+        out, idx, gate = _run_layer(w, x, res)
+        _check(cfg, 7, x, res, out, idx, gate)
+    w.top_k = 16
+    from dataclasses import replace
+    cfg16 = replace(cfg, top_k=16)
+    x = x_host(cfg, 8, batch=3)
+    res = residual_from_x(x)
+    out, idx, gate = _run_layer(w, x, res)
+    _check(cfg16, 7, x, res, out, idx, gate)
+
+
+def test_k3_batch1(k3_layer):
+    cfg = CONFIGS["k3_b1"]
+    for variant in (0, 1):
+        print(f"[case] layer K3 B1 seed 0 x-variant {variant}", flush=True)
+        x = x_host(cfg, 0, variant=variant)
+        res = residual_from_x(x)
+        out, idx, gate = _run_layer(k3_layer, x, res)
+        assert len(set(idx[0].tolist())) == 16
+        _check(cfg, 0, x, res, out, idx, gate)
+
+
+def test_k3_batch8(k3_layer):
+    cfg = CONFIGS["k3_b8"]
+    print("[case] layer K3 B8 seed 0", flush=True)
+    x = x_host(cfg, 0)
+    res = residual_from_x(x)
+    out, idx, gate = _run_layer(k3_layer, x, res)
+    _check(cfg, 0, x, res, out, idx, gate)
+
+
+def test_k3_batch64_zipf(k3_layer):
+    """Full-size batch 64 with the Zipf-like bias: every row's indices are
+    compared; outputs are compared on sampled rows."""
+    import torch
+    cfg = CONFIGS["k3_b64_zipf"]
+    print("[case] layer K3 B64 zipf seed 0", flush=True)
+    bias = _dev(synth.zipf_bias(0, 0, cfg.num_experts, cfg.zipf_s))
+    k3_layer.router_bias = bias
+    try:
+        x = x_host(cfg, 0)
+        res = residual_from_x(x)
+        out, idx, gate = _run_layer(k3_layer, x, res)
+    finally:
+        k3_layer.router_bias = None
+    hw = host_weights(cfg, 0)
+    lg, _ = oracle.router_logits(x, hw["router_w"], hw["router_bias"], cfg.hidden, cfg.num_experts)
+    idx_ref, gate_ref = oracle.topk(lg, cfg.top_k)
+    assert np.array_equal(idx, idx_ref)
+    assert np.abs(gate - gate_ref).max() <= 1e-6
+    counts = np.bincount(idx.ravel(), minlength=cfg.num_experts)
+    print(f"    distinct experts {int((counts > 0).sum())}, hottest {int(counts.max())} rows", flush=True)
+    _check(cfg, 0, x, res, out, idx, gate, rows=[0, 31, 63])
+
+
+def test_k3_deterministic(k3_layer):
+    import torch
+    cfg = CONFIGS["k3_b8"]
+    print("[case] layer K3 B8 determinism x20", flush=True)
+    x = _dev(x_host(cfg, 0, variant=3))
+    res0 = residual_from_x(x_host(cfg, 0, variant=3))
+    ws = moe.alloc_workspace(k3_layer, 8)
+    first = None
+    for _ in range(20):
+        r = _dev(res0.copy())
+        moe.moe_decode_layer(k3_layer, x, r, ws=ws)
+        out = r.cpu().numpy()
+        if first is None:
+            first = out
+        assert np.array_equal(out.view(np.uint32), first.view(np.uint32))
+
+
+def test_nan_scale_poisons_only_its_outputs():
+    import torch
+    cfg = CONFIGS["tiny"]
+    print("[case] layer tiny NaN scale", flush=True)
+    w = device_weights(cfg, 11)
+    x = x_host(cfg, 11)
+    res = residual_from_x(x)
+    out, idx, gate = _run_layer(w, x, res)
+    e = int(idx[0, 1])
+    nb = synth.expert_bytes(cfg.hidden, cfg.inter)
+    off = synth.expert_offsets(cfg.hidden, cfg.inter)
+    m = 17  # down-projection row m, block 0
+    w.experts[e * nb + off[5] + m * (cfg.inter // 32)] = 255
+    out2, idx2, _ = _run_layer(w, x, res)
+    assert np.array_equal(idx2, idx)
+    assert np.isnan(out2[0, m])
+    assert not np.any(np.isnan(np.delete(out2[0], m)))
