@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 MoE decode layer on one MI355X.
+
+Metric: microseconds per MoE layer and achieved HBM GB/s (fraction of the
+8 TB/s peak).  A step is one moe_decode_layer call -- router, top-k, shared
+expert, routed experts FC1/FC2 and the combine -- on one batch of synthetic
+rows of the K3-shaped layer (hidden 7168, 896 experts, top-16, intermediate
+1536, 17,547,264-byte MXFP4 experts, bf16 shared expert), batch 1.
+
+Cache hygiene: MI355X has 256 MB of last-level cache (MALL) and a step reads
+~360 MB, so consecutive steps rotate over `--layers` distinct copies of the
+layer (each 15.7 GB of experts) and over `--variants` input rows (different
+routing), so no step finds its weights in cache from an earlier step.
+Bytes are algorithmic: router + shared expert + U distinct experts (counted
+from each step's actual routing) + activations.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel -- the layer is a
+single persistent kernel, k_moe_layer -- timed with HIP events
+recorded by the library on the launch stream; `cpu_baseline` is the CPU
+oracle on one batch-1 layer (single thread).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+PEAK_GBPS = 8000.0
+METRIC = "µs per MoE layer and achieved HBM GB/s (% of peak) at batch 1/8/64"
+
+
+def layer_bytes(cfg, idx, with_bias: bool):
+    """Algorithmic HBM bytes of one layer step, total and per kernel."""
+    import numpy as np
+    import synth
+    H, I, E, k, Is = cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.shared_inter
+    B = idx.shape[0]
+    U = int(np.unique(idx).size)
+    nb = synth.expert_bytes(H, I)
+    router = E * H * 2 + (E * 4 if with_bias else 0)
+    shared = 3 * Is * H * 2
+    act = B * (H * 2 + 2 * H * 4)  # x read, residual read + write
+    total = router + shared + U * nb + act
+    # the layer is one kernel: its algorithmic bytes are the layer's
+    per_kernel = {"k_moe_layer": total}
+    return {"total": total, "U": U, "per_kernel": per_kernel}
+
+
+def run_config(cfg, layers, steps, warmup, variants, seed=0):
+    """Times `steps` layer steps. Returns a dict of measurements."""
+    import numpy as np
+    import torch
+
+    import memory_bound_mxfp4_amd as moe
+    from layer_inputs import residual_from_x, x_host
+    B = cfg.batch
+    names = moe.layer_kernel_names()
+    xs = [torch.from_numpy(x_host(cfg, seed, variant=v)).cuda() for v in range(variants)]
+    res0 = [torch.from_numpy(residual_from_x(x_host(cfg, seed, variant=v))).cuda() for v in range(variants)]
+    total = warmup + steps
+    res = [res0[s % variants].clone() for s in range(total)]
+    idx = torch.empty((total, B, cfg.top_k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((total, B, cfg.top_k), dtype=torch.float32, device="cuda")
+    ws = moe.alloc_workspace(layers[0], B)
+    bias = None
+    if cfg.zipf_s is not None:
+        import synth
+        bias = torch.from_numpy(synth.zipf_bias(seed, 0, cfg.num_experts, cfg.zipf_s)).cuda()
+    saved_bias = [w.router_bias for w in layers]
+    for w in layers:
+        w.router_bias = bias
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    try:
+        for s in range(warmup):
+            w = layers[s % len(layers)]
+            moe.moe_decode_layer(w, xs[s % variants], res[s], idx=idx[s], gate=gate[s], ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            s = warmup + i
+            w = layers[s % len(layers)]
+            moe.moe_decode_layer_timed(w, xs[s % variants], res[s], idx[s], gate[s], ws, events[i], stream=stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    finally:
+        for w, b in zip(layers, saved_bias):
+            w.router_bias = b
+    wall_s = t1 - t0
+    idx_h = idx[warmup:].cpu().numpy()
+    per = [layer_bytes(cfg, idx_h[i], bias is not None) for i in range(steps)]
+    tot_bytes = sum(p["total"] for p in per)
+    kern_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)]))
+               for j, n in enumerate(names)}
+    gpu_span_ms = events[0][0].elapsed_time(events[-1][-1])
+    kb = {n: float(np.mean([p["per_kernel"][n] for p in per])) for n in per[0]["per_kernel"]}
+    return {
+        "wall_s": wall_s,
+        "us_per_layer": wall_s / steps * 1e6,
+        "gpu_us_per_layer": gpu_span_ms / steps * 1e3,
+        "gbps": tot_bytes / wall_s / 1e9,
+        "bytes_per_layer": tot_bytes / steps,
+        "U_mean": float(np.mean([p["U"] for p in per])),
+        "kernel_us": {n: v * 1e3 for n, v in kern_ms.items()},
+        "kernel_bytes": kb,
+    }
+
+
+def cpu_baseline(seed=0):
+    """The oracle (single thread) on one K3-shaped batch-1 layer; expert regeneration excluded."""
+    import numpy as np
+    import oracle
+    from layer_inputs import host_experts, host_weights, residual_from_x, x_host
+    from synth import CONFIGS
+    cfg = CONFIGS["k3_b1"]
+    hw = host_weights(cfg, seed)
+    x = x_host(cfg, seed)
+    res = residual_from_x(x)
+    lg, _ = oracle.router_logits(x, hw["router_w"], None, cfg.hidden, cfg.num_experts)
+    idx, _ = oracle.topk(lg, cfg.top_k)
+    experts = host_experts(cfg, seed, idx.ravel())
+    t0 = time.perf_counter()
+    r = oracle.moe_layer(cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.shared_inter, hw["router_w"], None,
+                         hw["shared_gate"], hw["shared_up"], hw["shared_down"], experts, x, res)
+    dt = time.perf_counter() - t0
+    nbytes = layer_bytes(cfg, r["idx"], False)["total"]
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_layer": round(dt * 1e6, 1),
+            "sample": "one K3-shaped batch-1 layer (hidden 7168, 896 experts, top-16, seed 0), router + top-k + "
+                      "shared + 16 routed experts + combine, single thread; expert regeneration excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--layers", type=int, default=3, help="distinct layer copies rotated across steps")
+    ap.add_argument("--variants", type=int, default=32, help="distinct input rows rotated across steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the batch-8 and batch-64 lines")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the layer fits one MI355X; "
+              "this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from layer_inputs import device_weights
+    from synth import CONFIGS
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = CONFIGS["k3_b1"]
+    print(f"[bench] generating {args.layers} K3-shaped layers in HBM", file=sys.stderr, flush=True)
+    layers = [device_weights(cfg, 0, layer=l) for l in range(args.layers)]
+    print("[bench] timing batch 1", file=sys.stderr, flush=True)
+    main_r = run_config(cfg, layers, args.steps, args.warmup, args.variants)
+    extra = {}
+    if not args.no_extra:
+        for name in ("k3_b8", "k3_b64_zipf"):
+            print(f"[bench] timing {name}", file=sys.stderr, flush=True)
+            r = run_config(CONFIGS[name], layers, max(10, args.steps // 2), args.warmup, args.variants)
+            extra[name] = {"batch": CONFIGS[name].batch, "us_per_layer": round(r["us_per_layer"], 2),
+                           "gbps": round(r["gbps"], 1), "frac_peak": round(r["gbps"] / PEAK_GBPS, 4),
+                           "distinct_experts": round(r["U_mean"], 1),
+                           "kernel_us": {k: round(v, 2) for k, v in r["kernel_us"].items()}}
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+    fc1_bytes = main_r["kernel_bytes"]["k_moe_layer"]
+    fc1_us = main_r["kernel_us"]["k_moe_layer"]
+    achieved = fc1_bytes / (fc1_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(main_r["gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["us_per_layer"] / 1e3, 5),
+        "us_per_layer": round(main_r["us_per_layer"], 2),
+        "frac_peak": round(main_r["gbps"] / PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generator; weights ~N(0,0.02), MXFP4 experts, activations ~N(0,1))",
+        "config": {"workload": "K3-shaped MoE decode layer, batch 1: hidden 7168, 896 experts, top-16, "
+                               "expert intermediate 1536 (MXFP4, 17,547,264 B/expert), bf16 shared expert 1536, "
+                               "bf16 router", "batch": 1, "distinct_layers_rotated": args.layers,
+                   "input_variants": args.variants, "bytes_per_layer": int(main_r["bytes_per_layer"]),
+                   "distinct_experts": round(main_r["U_mean"], 1)},
+        "kernels_per_layer": len(main_r["kernel_us"]),
+        "kernel_us": {k: round(v, 2) for k, v in main_r["kernel_us"].items()},
+        "roofline": {"kernel": "k_moe_layer", "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(fc1_bytes), "avg_launch_us": round(fc1_us, 2)},
+        "cpu_baseline": cpu,
+        "extra_configs": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

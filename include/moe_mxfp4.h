@@ -141,18 +141,53 @@ moe_status expert_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int n,
                              moe_dtype x_dtype, int batch, float* y, void* stream);
 
 /*
- * moe_decode_layer -- the whole layer for `batch` rows.
+ * moe_workspace_init -- clear a workspace before its first use.
+ * The first bytes of a layer workspace are a control block of counters that
+ * moe_decode_layer's single persistent kernel synchronises on.  It must be
+ * zero when a call starts; every call leaves it zero again when it ends, so
+ * a workspace needs this (or any zero fill of the whole buffer) once after
+ * allocation, and again only after a call that did not complete (a device
+ * fault).  Enqueued on `stream`.  ws 256-byte aligned, ws_bytes a multiple
+ * of 16.
+ * The uint32 at byte offset MOE_WS_STATUS_OFFSET of the workspace is a sticky
+ * status word: nonzero means a synchronisation wait inside a call timed out
+ * (about a second), which only happens if the control block was not zero at
+ * the start of a call; the outputs of such a call are not valid.  It is
+ * cleared by moe_workspace_init.
+ */
+#define MOE_WS_STATUS_OFFSET 28
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_decode_layer -- the whole layer for `batch` rows, as one kernel launch.
  *   x          bf16 [batch][hidden], the layer input (normalised activations)
  *   residual   fp32 [batch][hidden], read and overwritten with
  *              residual + shared + sum_j gate_j * expert_j; must not alias x
  *   topk_idx   out int32 [batch][top_k]; topk_gate out fp32 [batch][top_k]
  *   ws         workspace of >= moe_workspace_size(w, batch) bytes, 256-byte
- *              aligned, owned by the caller; its contents on entry are
- *              ignored (the library clears what it needs)
+ *              aligned, owned by the caller, cleared once by
+ *              moe_workspace_init; calls that share a workspace must be
+ *              ordered on one stream (they must not overlap)
  * Routing never leaves the device: no host synchronisation happens inside.
  */
 moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
                             int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Per-kernel timing of moe_decode_layer (for profiling and benchmarks).
+ * moe_decode_layer_kernel_count() is the number K of kernels one call
+ * launches; moe_decode_layer_kernel_name(i) the name of the i-th (NULL out
+ * of range).  moe_decode_layer_timed() is moe_decode_layer that also records
+ * K+1 caller-created hipEvent_t `events` on `stream`: events[0] before the
+ * first kernel and events[i+1] right after kernel i, so the elapsed time
+ * between events[i] and events[i+1] brackets kernel i.  n_events must be at
+ * least K+1 and no entry may be NULL (else MOE_ERR_INVALID_ARGUMENT).
+ */
+int moe_decode_layer_kernel_count(void);
+const char* moe_decode_layer_kernel_name(int i);
+moe_status moe_decode_layer_timed(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                                  int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream,
+                                  void* const* events, int n_events);
 
 /*
  * Dense-block pieces used between MoE layers of a decode-step stack.

@@ -22,7 +22,8 @@ MAX_BATCH = 64
 
 # Symbols the C header declares (checked by tests/test_abi.py).
 EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size", "router_topk",
-           "expert_gemv_mxfp4", "moe_decode_layer", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16",
+           "expert_gemv_mxfp4", "moe_decode_layer", "moe_decode_layer_kernel_count",
+           "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16",
            "moe_status_string")
 
 
@@ -60,6 +61,10 @@ def load():
         "router_topk": (I, [P, I, I, P, P, I, I, P, P, P, P, Z, P]),
         "expert_gemv_mxfp4": (I, [P, P, I, I, P, I, I, P, P]),
         "moe_decode_layer": (I, [P, P, P, I, P, P, P, Z, P]),
+        "moe_decode_layer_kernel_count": (I, []),
+        "moe_decode_layer_kernel_name": (ctypes.c_char_p, [I]),
+        "moe_decode_layer_timed": (I, [P, P, P, I, P, P, P, Z, P, P, I]),
+        "moe_workspace_init": (I, [P, Z, P]),
         "rmsnorm_bf16": (I, [P, I, I, F, P, P]),
         "dense_gemv_bf16": (I, [P, I, I, P, I, P, P]),
         "residual_add_bf16": (I, [P, P, I, I, P]),
@@ -112,10 +117,20 @@ class LayerWeights:
     shared_up: Optional[object] = None
     shared_down: Optional[object] = None
 
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        if name != "_cs":
+            object.__setattr__(self, "_cs", None)
+
     def c_struct(self) -> LayerWeightsC:
-        return LayerWeightsC(self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter,
+        cs = getattr(self, "_cs", None)
+        if cs is not None:
+            return cs
+        cs = LayerWeightsC(self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter,
                              _ptr(self.router_w), _ptr(self.router_bias), _ptr(self.shared_gate),
                              _ptr(self.shared_up), _ptr(self.shared_down), _ptr(self.experts))
+        object.__setattr__(self, "_cs", cs)
+        return cs
 
 
 def workspace_size(w: LayerWeights, batch: int) -> int:
@@ -125,9 +140,26 @@ def workspace_size(w: LayerWeights, batch: int) -> int:
     return int(n.value)
 
 
+WS_STATUS_OFFSET = 28
+
+
+def workspace_init(ws, stream=None):
+    """Clear a workspace before its first use (moe_workspace_init)."""
+    _check(load().moe_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "moe_workspace_init")
+    return ws
+
+
 def alloc_workspace(w: LayerWeights, batch: int, device=None):
+    """A cleared workspace for `w` at `batch` rows."""
     import torch
-    return torch.empty(workspace_size(w, batch), dtype=torch.uint8, device=device or w.router_w.device)
+    ws = torch.empty(workspace_size(w, batch), dtype=torch.uint8, device=device or w.router_w.device)
+    return workspace_init(ws)
+
+
+def workspace_status(ws) -> int:
+    """The workspace's sticky status word (0 = every wait completed). Synchronises."""
+    import numpy as np
+    return int(ws[WS_STATUS_OFFSET:WS_STATUS_OFFSET + 4].cpu().numpy().view(np.uint32)[0])
 
 
 def router_topk(x, router_w, top_k: int, bias=None, idx=None, gate=None, logits=None, ws=None, stream=None):
@@ -168,6 +200,26 @@ def moe_decode_layer(w: LayerWeights, x, residual, idx=None, gate=None, ws=None,
     cs = w.c_struct()
     _check(load().moe_decode_layer(ctypes.byref(cs), _ptr(x), _ptr(residual), B, _ptr(idx), _ptr(gate), _ptr(ws),
                                    ws.numel(), _stream(stream)), "moe_decode_layer")
+    return idx, gate
+
+
+def layer_kernel_names():
+    lib = load()
+    return [lib.moe_decode_layer_kernel_name(i).decode() for i in range(lib.moe_decode_layer_kernel_count())]
+
+
+def moe_decode_layer_timed(w: LayerWeights, x, residual, idx, gate, ws, events, stream=None):
+    """moe_decode_layer recording torch.cuda.Event objects around each kernel
+    (len(events) == len(layer_kernel_names()) + 1) on `stream`."""
+    B = x.shape[0]
+    cs = w.c_struct()
+    for e in events:  # torch creates the underlying hipEvent_t lazily, on first record
+        if not e.cuda_event:
+            e.record()
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check(load().moe_decode_layer_timed(ctypes.byref(cs), _ptr(x), _ptr(residual), B, _ptr(idx), _ptr(gate),
+                                         _ptr(ws), ws.numel(), _stream(stream), arr, len(events)),
+           "moe_decode_layer_timed")
     return idx, gate
 
 

@@ -33,6 +33,9 @@ Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B) {
   Workspace w;
   const size_t slots = (size_t)B * k;
   const size_t umax = slots < (size_t)E ? slots : (size_t)E;
+  w.umax = (int)umax;
+  w.ctrl_words = (CTRL_FC1 + (int)umax + layer_tiles_fc2(H)) * CTRL_STRIDE;
+  w.ctrl = reinterpret_cast<unsigned*>(take(sizeof(unsigned) * (size_t)w.ctrl_words));
   w.logits = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * E));
   w.sched.n_active = reinterpret_cast<int*>(take(sizeof(int)));
   w.sched.active = reinterpret_cast<int*>(take(sizeof(int) * umax));
@@ -137,8 +140,15 @@ moe_status expert_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int n,
   return MOE_OK;
 }
 
-moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
-                            int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// The kernels moe_decode_layer launches, in launch order.
+static const char* const kLayerKernels[] = {"k_moe_layer"};
+static const int kNumLayerKernels = 1;
+
+static moe_status run_layer(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                            int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, hipStream_t s,
+                            void* const* events) {
   moe_status st = check_layer(w, batch);
   if (st != MOE_OK) return st;
   if (!x || !residual || !topk_idx || !topk_gate || !ws) return MOE_ERR_INVALID_ARGUMENT;
@@ -146,11 +156,6 @@ moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float
   const int H = w->hidden, I = w->inter, E = w->num_experts, k = w->top_k, Is = w->shared_inter;
   Workspace wsl = ws_layout(ws, H, I, E, k, Is, batch);
   if (ws_bytes < wsl.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_router_logits(x, batch, H, w->router_w, w->router_bias, E, wsl.logits, s) != hipSuccess)
-    return MOE_ERR_HIP;
-  if (launch_topk(wsl.logits, batch, E, k, topk_idx, topk_gate, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_schedule(topk_idx, batch, k, E, wsl.sched, s) != hipSuccess) return MOE_ERR_HIP;
   LayerArgs a;
   a.H = H;
   a.I = I;
@@ -167,7 +172,42 @@ moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float
   a.gate = topk_gate;
   a.ws = wsl;
   a.residual = residual;
-  if (launch_experts(a, s) != hipSuccess) return MOE_ERR_HIP;
+  int ev = 0;
+  auto mark = [&]() {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[ev++]), s) == hipSuccess;
+  };
+  if (!mark()) return MOE_ERR_HIP;
+  if (launch_layer(a, w->router_bias, w->router_w, topk_idx, s) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                            int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
+  return run_layer(w, x, residual, batch, topk_idx, topk_gate, ws, ws_bytes, static_cast<hipStream_t>(stream),
+                   nullptr);
+}
+
+int moe_decode_layer_kernel_count(void) { return kNumLayerKernels; }
+
+const char* moe_decode_layer_kernel_name(int i) {
+  return (i >= 0 && i < kNumLayerKernels) ? kLayerKernels[i] : nullptr;
+}
+
+moe_status moe_decode_layer_timed(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                                  int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream,
+                                  void* const* events, int n_events) {
+  if (!events || n_events < kNumLayerKernels + 1) return MOE_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i <= kNumLayerKernels; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARGUMENT;
+  return run_layer(w, x, residual, batch, topk_idx, topk_gate, ws, ws_bytes, static_cast<hipStream_t>(stream),
+                   events);
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned(ws, 256) || ws_bytes % 16) return MOE_ERR_INVALID_ARGUMENT;
+  if (launch_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
 

@@ -32,8 +32,31 @@ struct Sched {
   int* rows;
 };
 
+// Control block at the start of the workspace: counters of uint32, each on a
+// 128-byte line of its own (counter i at word CTRL_STRIDE * i), so that polls
+// of different counters never share a cache line.  Zeroed once by
+// moe_workspace_init; every layer call leaves it zeroed again, except the
+// sticky error word.
+constexpr int CTRL_STRIDE = 32;
+enum {
+  CTRL_HEAD = 0,     // work-queue head
+  CTRL_ROUTER = 1,   // router units done
+  CTRL_ROUTING = 2,  // routing units done
+  CTRL_READY = 3,    // routing published (0/1)
+  CTRL_U = 4,        // number of distinct experts
+  CTRL_SH1 = 5,      // shared FC1 units done
+  CTRL_EXIT = 6,     // workgroups that have exited
+  CTRL_ERR = 7,      // sticky: a bounded wait expired (byte offset 28: in the first line)
+  CTRL_FC1 = 8       // [umax] routed FC1 units done per active expert, then [T2] FC2 tile tickets
+};
+// Word index of counter i (the error word stays at word 7 of the first line).
+__host__ __device__ constexpr int ctrl_word(int i) { return i == CTRL_ERR ? CTRL_ERR : i * CTRL_STRIDE; }
+
 // Workspace of moe_decode_layer.
 struct Workspace {
+  unsigned* ctrl;
+  int ctrl_words;
+  int umax;
   float* logits;    // [B][E]
   Sched sched;
   float* h_shared;  // [B][Is]
@@ -48,7 +71,6 @@ Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B);
 hipError_t launch_router_logits(const uint16_t* x, int B, int H, const uint16_t* wr, const float* bias, int E,
                                 float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, int B, int E, int k, int32_t* idx, float* gate, hipStream_t s);
-hipError_t launch_schedule(const int32_t* idx, int B, int k, int E, Sched sched, hipStream_t s);
 
 struct LayerArgs {
   int H, I, E, k, Is, B;
@@ -60,7 +82,9 @@ struct LayerArgs {
   Workspace ws;
   float* residual;
 };
-hipError_t launch_experts(const LayerArgs& a, hipStream_t s);
+hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* wr, int32_t* idx, hipStream_t s);
+int layer_tiles_fc2(int H);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 hipError_t launch_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int N, int K, const void* x, bool x_f32,
                              int B, float* y, hipStream_t s);

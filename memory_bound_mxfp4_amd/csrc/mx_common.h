@@ -22,6 +22,21 @@ __device__ __forceinline__ u32x4 ld_weight16(const void* p) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Coherent (agent-scope) scalar loads and stores.  Data one workgroup of a
+// launch writes and another reads goes through these: on gfx950 they carry
+// the sc1 cache policy, i.e. they are performed at the device coherence point
+// instead of in an XCD's non-coherent L2, so no L2 write-back or invalidate
+// (which serialise device-wide) is ever needed to hand data between
+// workgroups on different XCDs.
+template <typename T>
+__device__ __forceinline__ void st_coh(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coh(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // E8M0 scale byte -> an fp32 power of two for the gfx950 scaled FP4
 // conversions, which take the exponent of their scale operand: 2^(b-127),
 // with 2^-127 (byte 0) as a subnormal and NaN for byte 0xFF.

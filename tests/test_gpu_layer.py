@@ -131,6 +131,31 @@ def test_k3_deterministic(k3_layer):
         assert np.array_equal(out.view(np.uint32), first.view(np.uint32))
 
 
+def test_workspace_reuse_and_status(k3_layer):
+    """One workspace serves many calls (its control block is left cleared),
+    across batch sizes it is large enough for, with no wait timing out."""
+    import torch
+    print("[case] layer K3 workspace reuse B8 -> B1 -> B8", flush=True)
+    ws = moe.alloc_workspace(k3_layer, 8)
+    for cfg_name, variant in (("k3_b8", 5), ("k3_b1", 6), ("k3_b8", 7), ("k3_b1", 6)):
+        cfg = CONFIGS[cfg_name]
+        x = x_host(cfg, 0, variant=variant)
+        res = residual_from_x(x)
+        r = _dev(res.copy())
+        idx, gate = moe.moe_decode_layer(k3_layer, _dev(x), r, ws=ws)
+        torch.cuda.synchronize()
+        assert moe.workspace_status(ws) == 0
+        assert np.all(ws[:64].cpu().numpy() == 0)  # control block cleared again
+        ref_idx = oracle_layer_idx(cfg, x)
+        assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+def oracle_layer_idx(cfg, x):
+    hw = host_weights(cfg, 0)
+    lg, _ = oracle.router_logits(x, hw["router_w"], hw["router_bias"], cfg.hidden, cfg.num_experts)
+    return oracle.topk(lg, cfg.top_k)[0]
+
+
 def test_nan_scale_poisons_only_its_outputs():
     import torch
     cfg = CONFIGS["tiny"]
@@ -148,3 +173,23 @@ def test_nan_scale_poisons_only_its_outputs():
     assert np.array_equal(idx2, idx)
     assert np.isnan(out2[0, m])
     assert not np.any(np.isnan(np.delete(out2[0], m)))
+
+
+def test_timed_entry_point_matches_untimed():
+    import torch
+    cfg = CONFIGS["tiny"]
+    print("[case] layer tiny timed vs untimed", flush=True)
+    w = device_weights(cfg, 12)
+    x = x_host(cfg, 12, batch=4)
+    res = residual_from_x(x)
+    out, idx, gate = _run_layer(w, x, res)
+    names = moe.layer_kernel_names()
+    assert names == ["k_moe_layer"]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    r = _dev(res.copy())
+    idx2 = torch.empty_like(torch.from_numpy(idx)).cuda()
+    gate2 = torch.empty_like(torch.from_numpy(gate)).cuda()
+    moe.moe_decode_layer_timed(w, _dev(x), r, idx2, gate2, moe.alloc_workspace(w, 4), events)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.cpu().numpy(), out) and np.array_equal(idx2.cpu().numpy(), idx)
+    assert all(events[i].elapsed_time(events[i + 1]) >= 0 for i in range(len(names)))
