@@ -34,7 +34,7 @@ Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B) {
   const size_t slots = (size_t)B * k;
   const size_t umax = slots < (size_t)E ? slots : (size_t)E;
   w.umax = (int)umax;
-  w.ctrl_words = (CTRL_FC1 + (int)umax + layer_tiles_fc2(H)) * CTRL_STRIDE;
+  w.ctrl_words = ctrl_lines((int)umax, layer_tiles_fc2(H)) * CTRL_STRIDE;
   w.ctrl = reinterpret_cast<unsigned*>(take(sizeof(unsigned) * (size_t)w.ctrl_words));
   w.logits = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * E));
   w.sched.n_active = reinterpret_cast<int*>(take(sizeof(int)));

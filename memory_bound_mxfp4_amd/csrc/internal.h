@@ -40,15 +40,21 @@ struct Sched {
 constexpr int CTRL_STRIDE = 32;
 enum {
   CTRL_HEAD = 0,     // work-queue head
-  CTRL_ROUTER = 1,   // router units done
-  CTRL_ROUTING = 2,  // routing units done
-  CTRL_READY = 3,    // routing published (0/1)
-  CTRL_U = 4,        // number of distinct experts
+  CTRL_ROUTER = 1,   // (unused)
+  CTRL_ROUTING = 2,  // rows routed (batch > 1)
+  CTRL_READY = 3,    // schedule published (0/1, batch > 1)
+  CTRL_U = 4,        // number of distinct experts (batch > 1)
   CTRL_SH1 = 5,      // shared FC1 units done
   CTRL_EXIT = 6,     // workgroups that have exited
   CTRL_ERR = 7,      // sticky: a bounded wait expired (byte offset 28: in the first line)
-  CTRL_FC1 = 8       // [umax] routed FC1 units done per active expert, then [T2] FC2 tile tickets
+  CTRL_FC1 = 8       // first of the per-launch arrays below
 };
+// Counter lines after CTRL_FC1: [umax] routed FC1 units done per active expert
+// (per slot at batch 1), [T2] FC2 tile tickets, [MOE_MAX_BATCH] router
+// row-block tickets, [MOE_MAX_TOPK] published expert + 1 of each slot (batch 1).
+__host__ __device__ constexpr int ctrl_lines(int umax, int T2) {
+  return CTRL_FC1 + umax + T2 + MOE_MAX_BATCH + MOE_MAX_TOPK;
+}
 // Word index of counter i (the error word stays at word 7 of the first line).
 __host__ __device__ constexpr int ctrl_word(int i) { return i == CTRL_ERR ? CTRL_ERR : i * CTRL_STRIDE; }
 

@@ -43,13 +43,17 @@
 #include "internal.h"
 #include "moe_device.h"
 
+#include <algorithm>
+
 namespace moe {
 
-constexpr int NT1 = 32;   // routed FC1 rows (of I) per unit: 32 x 7 KB of codes at H 7168
-constexpr int NTS1 = 4;   // shared FC1 rows (of Is) per unit: 4 x 28 KB of bf16
-constexpr int NT2 = 256;  // FC2 tile (rows of H) of the combine; routed FC2 unit = one tile
-constexpr int NTS2 = 64;  // shared FC2 rows per unit (NT2 / NTS2 units per tile)
-constexpr int SUB2 = NT2 / NTS2;
+constexpr int NT1 = 16;   // routed FC1 rows (of I) per unit: 16 x 2 x 3.8 KB at H 7168
+constexpr int NTS1 = 4;   // shared FC1 rows (of Is) per unit: 4 x 2 x 14 KB of bf16
+constexpr int NT2 = 256;  // FC2 tile (rows of H): the combine's granularity
+constexpr int NTS2 = 32;  // shared FC2 rows per unit
+constexpr int NTR2 = 128; // routed FC2 rows per unit
+constexpr int SUB2 = NT2 / NTS2;  // shared FC2 units per tile
+constexpr int SUBR = NT2 / NTR2;  // routed FC2 units per tile and expert
 constexpr int CPL1 = 7;   // FC1: 16-byte chunks per lane per pass (half-wave rows)
 constexpr int CPL2 = 6;   // FC2: 16-byte chunks per lane per pass (8 lanes per row)
 constexpr int MAX_ROWS = MOE_MAX_BATCH;    // activation rows one expert can have
@@ -79,7 +83,8 @@ struct LayerParams {
   int umax;
   int n_rt_e;  // router expert pairs (2 experts per unit, 2 waves per expert)
   int n_rt;    // router units = n_rt_e * row blocks
-  int n_ro;    // routing units (one row each)
+  int n_rb;    // router row blocks
+  int n_static;  // units 0 .. n_static-1 go to workgroups 0 .. n_static-1
   int n_s1;    // shared FC1 units
   int T1;      // routed FC1 tiles per expert
   int T2;      // FC2 tiles over H (the combine's granularity)
@@ -154,6 +159,7 @@ struct Lds {  // static LDS of the kernel
   int flag;        // "this workgroup is the last arriver"
   int wtot[8];     // scan scratch
   int nrows;       // rows of the current unit
+  int expert;      // expert of the current routed unit (batch 1)
   double part[4][4];  // router: partial sums of the second half-row waves [wave][row]
   int slot[MAX_ROWS];  // slot ids (routed) or batch rows (shared) of the current unit
 };
@@ -563,43 +569,22 @@ struct Fc2Bf {
 
 // ---- units --------------------------------------------------------------------
 
-// Router unit: experts 2u and 2u+1 for a block of rows.  Waves 0-1 take the
-// two halves of expert 2u's row, waves 2-3 those of expert 2u+1, so every wave
-// streams 7 KB at H 7168 in one pass of loads; the halves meet in LDS.
-template <int RG>
-__device__ void router_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int u) {
-  const int pe = u % p.n_rt_e, rb = u / p.n_rt_e;
-  const int b0 = rb * RG, nr = min(RG, p.B - b0);
-  load_rows(p, st, L, -1);
-  stage_x(p, st, L, xs, false, b0, nr);
-  const int w = threadIdx.x >> 6, half = w & 1;
-  const int e = 2 * pe + (w >> 1);
-  const int C = p.H / 8, gh = (C + 1) / 2;
-  double acc[RG];
-  router_dot<RG>(p.wr + (size_t)min(e, p.E - 1) * p.H, half * gh, half ? C : gh, xs, p.xstride, nr, acc);
-  if (half && (threadIdx.x & 63) == 0) {
-#pragma unroll
-    for (int r = 0; r < RG; ++r) L.part[w][r] = acc[r];
-  }
-  __syncthreads();
-  if (!half && e < p.E && (threadIdx.x & 63) == 0) {
-    const double bb = p.bias ? (double)p.bias[e] : 0.0;
-#pragma unroll
-    for (int r = 0; r < RG; ++r)
-      if (r < nr) st_coh(p.logits + (size_t)(b0 + r) * p.E + e, (float)(acc[r] + L.part[w + 1][r] + bb));
-  }
-  wg_signal_add((p.ctrl + ctrl_word(CTRL_ROUTER)));
+__device__ __forceinline__ unsigned* ctrl_at(const LayerParams& p, int line) { return p.ctrl + ctrl_word(line); }
+__device__ __forceinline__ int line_fc1(int a) { return CTRL_FC1 + a; }
+__device__ __forceinline__ int line_tile(const LayerParams& p, int t) { return CTRL_FC1 + p.umax + t; }
+__device__ __forceinline__ int line_rb(const LayerParams& p, int rb) { return CTRL_FC1 + p.umax + p.T2 + rb; }
+__device__ __forceinline__ int line_pub(const LayerParams& p, int j) {
+  return CTRL_FC1 + p.umax + p.T2 + MOE_MAX_BATCH + j;
 }
 
 // Expert-gathered schedule from idx[B][k] (LDS counting; 256 threads).
 // LDS: cnt[E], start[E], ids[B*k].
-// ids_ready: the slots' expert ids are already in LDS ids[] (batch 1).
-__device__ void build_schedule(const LayerParams& p, int* cnt, int* wtot /* LDS [8] */, bool ids_ready) {
+__device__ void build_schedule(const LayerParams& p, int* cnt, int* wtot /* LDS [8] */) {
   int* start = cnt + p.E;
   int* ids = start + p.E;
   const int t = threadIdx.x, nslots = p.B * p.k;
   // every slot's expert id, coherent loads in batches of 4 per thread
-  for (int base = t; !ids_ready && base < nslots; base += 256 * 4) {
+  for (int base = t; base < nslots; base += 256 * 4) {
     int v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = ld_coh(p.idx + min(base + 256 * i, nslots - 1));
@@ -655,7 +640,7 @@ __device__ void build_schedule(const LayerParams& p, int* cnt, int* wtot /* LDS 
   }
   if (t == 255) {
     st_coh(p.row_off + base_a + ia, base_r + ir);
-    __hip_atomic_store((p.ctrl + ctrl_word(CTRL_U)), (unsigned)(base_a + ia), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_coh(ctrl_at(p, CTRL_U), (unsigned)(base_a + ia));
   }
   __syncthreads();
   for (int s = t; s < nslots; s += 256) {
@@ -664,35 +649,101 @@ __device__ void build_schedule(const LayerParams& p, int* cnt, int* wtot /* LDS 
   }
 }
 
-// Routing keeps its working set (top-k keys, slot ids) in LDS: it runs only a
-// few times per call, and holding that state in registers would set the
-// register budget -- and so the occupancy -- of the whole kernel.  With one
-// row there is one routing unit: it keeps its k expert ids in LDS and builds
-// the schedule at once, without a counter round trip or reloading idx.
+// Routing of rows [b0, b0+nr), run by the workgroup that completed their
+// logits.  Top-k keys and candidates live in LDS (the x region): routing runs
+// a handful of times per call, and holding its state in registers would set
+// the register budget -- and so the occupancy -- of the whole kernel.
+//   batch 1: each selected expert is published at once in its slot's counter
+//            line (expert + 1), which is all a routed unit needs;
+//   batch > 1: the workgroup that routes the last rows inverts the routing
+//            into the expert-gathered schedule and publishes READY.
 template <int TPL>
-__device__ void routing_unit(const LayerParams& p, WgState& st, Lds& L, int* lds_ints, int b) {
-  wg_wait_geq(p, (p.ctrl + ctrl_word(CTRL_ROUTER)), (unsigned)p.n_rt);
+__device__ void route_rows(const LayerParams& p, WgState& st, Lds& L, int* lds_ints, int b0, int nr) {
   __builtin_amdgcn_s_setprio(3);  // on the critical path: issue ahead of streaming waves
-  __syncthreads();                // the LDS x region is reused for the candidates
-  const int myx = topk_row_wg<TPL>(p.logits + (size_t)b * p.E, p.E, p.k, reinterpret_cast<uint32_t*>(lds_ints),
-                                   p.idx + (size_t)b * p.k, p.gate + (size_t)b * p.k);
+  for (int r = 0; r < nr; ++r) {
+    __syncthreads();  // the LDS region is reused
+    const int b = b0 + r;
+    const int myx = topk_row_wg<TPL>(p.logits + (size_t)b * p.E, p.E, p.k, reinterpret_cast<uint32_t*>(lds_ints),
+                                     p.idx + (size_t)b * p.k, p.gate + (size_t)b * p.k);
+    if (p.B == 1 && threadIdx.x < p.k) {
+      __builtin_amdgcn_s_waitcnt(0);  // this lane's idx and gate stores are complete
+      st_coh(ctrl_at(p, line_pub(p, threadIdx.x)), (unsigned)myx + 1u);
+    }
+  }
   st.x_cached = false;
-  if (p.n_ro == 1) {
-    __syncthreads();  // candidate keys no longer read
-    if (threadIdx.x < p.k) lds_ints[2 * p.E + threadIdx.x] = myx;
+  if (p.B > 1) {
+    const unsigned old = wg_signal_add(ctrl_at(p, CTRL_ROUTING));
+    if (threadIdx.x == 0) L.flag = (old == (unsigned)p.n_rb - 1);
     __syncthreads();
-    build_schedule(p, lds_ints, L.wtot, true);
-    wg_signal_add((p.ctrl + ctrl_word(CTRL_READY)));
-  } else {
-    const unsigned old = wg_signal_add((p.ctrl + ctrl_word(CTRL_ROUTING)));
-    if (threadIdx.x == 0) L.flag = (old == (unsigned)p.n_ro - 1);
-    __syncthreads();
-    if (L.flag) {  // the last routing unit inverts the routing
-      build_schedule(p, lds_ints, L.wtot, false);
-      wg_signal_add((p.ctrl + ctrl_word(CTRL_READY)));
+    if (L.flag) {
+      build_schedule(p, lds_ints, L.wtot);
+      wg_signal_add(ctrl_at(p, CTRL_READY));
     }
   }
   __builtin_amdgcn_s_setprio(0);
+}
+
+// Router unit: experts 2u and 2u+1 for a block of rows.  Waves 0-1 take the
+// two halves of expert 2u's row, waves 2-3 those of expert 2u+1, so every wave
+// streams 7 KB at H 7168 in one pass of loads; the halves meet in LDS.  The
+// last unit of a row block to finish routes its rows.
+template <int RG, int TPL>
+__device__ void router_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int u) {
+  const int pe = u % p.n_rt_e, rb = u / p.n_rt_e;
+  const int b0 = rb * RG, nr = min(RG, p.B - b0);
+  load_rows(p, st, L, -1);
+  stage_x(p, st, L, xs, false, b0, nr);
+  const int w = threadIdx.x >> 6, half = w & 1;
+  const int e = 2 * pe + (w >> 1);
+  const int C = p.H / 8, gh = (C + 1) / 2;
+  double acc[RG];
+  router_dot<RG>(p.wr + (size_t)min(e, p.E - 1) * p.H, half * gh, half ? C : gh, xs, p.xstride, nr, acc);
+  if (half && (threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) L.part[w][r] = acc[r];
+  }
+  __syncthreads();
+  if (!half && e < p.E && (threadIdx.x & 63) == 0) {
+    const double bb = p.bias ? (double)p.bias[e] : 0.0;
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+      if (r < nr) st_coh(p.logits + (size_t)(b0 + r) * p.E + e, (float)(acc[r] + L.part[w + 1][r] + bb));
+  }
+  const unsigned old = wg_signal_add(ctrl_at(p, line_rb(p, rb)));
+  if (threadIdx.x == 0) L.flag = (old == (unsigned)p.n_rt_e - 1);
+  __syncthreads();
+  if (L.flag) route_rows<TPL>(p, st, L, reinterpret_cast<int*>(xs), b0, nr);
+}
+
+// Batch 1: wait until slot a's expert is published (and, if fc1_target > 0,
+// until that many FC1 units of the slot are done); both counters are read in
+// one round trip per poll.  Sets the unit's row list to the slot itself.
+__device__ __forceinline__ int wait_slot(const LayerParams& p, Lds& L, int a, unsigned fc1_target) {
+  if (threadIdx.x == 0) {
+    const unsigned* pub = ctrl_at(p, line_pub(p, a));
+    const unsigned* done = ctrl_at(p, line_fc1(a));
+    unsigned it = 0, nap = 1, v;
+    for (;;) {
+      v = ld_ctrl(pub);
+      const unsigned c = fc1_target ? ld_ctrl(done) : 0u;
+      if (v != 0u && c >= fc1_target) break;
+      if (nap <= 1) __builtin_amdgcn_s_sleep(1);
+      else if (nap <= 4) __builtin_amdgcn_s_sleep(4);
+      else __builtin_amdgcn_s_sleep(16);
+      nap = nap < 32 ? 2 * nap : 32;
+      if (++it >= SPIN_LIMIT) {
+        __hip_atomic_fetch_or(ctrl_at(p, CTRL_ERR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = 1u;
+        break;
+      }
+    }
+    L.expert = (int)min(v - 1u, (unsigned)p.E - 1u);
+    L.slot[0] = a;
+    L.nrows = 1;
+  }
+  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return L.expert;
 }
 
 template <int RG, bool FULL>
@@ -702,7 +753,6 @@ __device__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
   load_rows(p, st, L, -1);
   for (int g0 = 0; g0 < p.B; g0 += RG) {
     const int nr = min(RG, p.B - g0);
-    stage_x(p, st, L, xs, false, g0, nr);
     Fc1Bf<RG, FULL> f;
     f.w = half ? p.su : p.sg;
     f.H = p.H;
@@ -717,21 +767,30 @@ __device__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.out_ld = p.Is;
     f.row = L.slot + g0;
     const int nrows = f.n0 < n_end ? (n_end - f.n0 + 3) / 4 : 0;
-    run_passes<BfBuf<CPL1>>(f, nrows * f.nseg);
+    const int P = nrows * f.nseg;
+    BfBuf<CPL1> ba, bb;
+    prime_passes(f, P, ba, bb);
+    stage_x(p, st, L, xs, false, g0, nr);
+    drive_passes(f, P, ba, bb);
   }
-  wg_signal_add((p.ctrl + ctrl_word(CTRL_SH1)));
+  wg_signal_add(ctrl_at(p, CTRL_SH1));
 }
 
 template <int RG, bool FULL>
 __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int t) {
-  load_rows(p, st, L, a);
+  int expert;
+  if (p.B == 1) {
+    expert = wait_slot(p, L, a, 0u);
+  } else {
+    load_rows(p, st, L, a);
+    expert = st.s_active[a];
+  }
   const int nrows_unit = L.nrows;
-  const uint8_t* blob = p.experts + (size_t)st.s_active[a] * p.blob_bytes;
+  const uint8_t* blob = p.experts + (size_t)expert * p.blob_bytes;
   const int half = (threadIdx.x & 63) >> 5;
   const int n_begin = t * NT1, n_end = min(p.I, n_begin + NT1);
   for (int g0 = 0; g0 < nrows_unit; g0 += RG) {
     const int nr = min(RG, nrows_unit - g0);
-    stage_x(p, st, L, xs, true, g0, nr);
     Fc1Mx<RG, FULL> f;
     f.codes = blob + p.off[half];
     f.scales = blob + p.off[3 + half];
@@ -747,16 +806,20 @@ __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.out_ld = p.I;
     f.slot = L.slot + g0;
     const int nrows = f.n0 < n_end ? (n_end - f.n0 + 3) / 4 : 0;
-    run_passes<MxBuf<CPL1>>(f, nrows * f.nseg);
+    const int P = nrows * f.nseg;
+    MxBuf<CPL1> ba, bb;
+    prime_passes(f, P, ba, bb);
+    stage_x(p, st, L, xs, true, g0, nr);
+    drive_passes(f, P, ba, bb);
   }
-  wg_signal_add((p.ctrl + ctrl_word(CTRL_FC1 + a)));
+  wg_signal_add(ctrl_at(p, line_fc1(a)));
 }
 
 // After a FC2 unit of tile t: count it; the last contribution folds the tile
 // into the residual (fixed order: shared, then j = 0..k-1).
 __device__ void fc2_ticket(const LayerParams& p, int U, Lds& L, int t) {
-    const unsigned expected = (unsigned)((p.Is > 0 ? SUB2 : 0) + U);
-  const unsigned old = wg_signal_add(p.ctrl + ctrl_word(CTRL_FC1 + p.umax + t));
+  const unsigned expected = (unsigned)((p.Is > 0 ? SUB2 : 0) + SUBR * U);
+  const unsigned old = wg_signal_add(ctrl_at(p, line_tile(p, t)));
   if (threadIdx.x == 0) L.flag = (old == expected - 1);
   __syncthreads();
   if (!L.flag) return;
@@ -783,13 +846,11 @@ __device__ void fc2_ticket(const LayerParams& p, int U, Lds& L, int t) {
 
 template <int RG, bool FULL>
 __device__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int v) {
-  wg_wait_geq(p, (p.ctrl + ctrl_word(CTRL_SH1)), (unsigned)p.n_s1);
-  load_rows(p, st, L, -1);
   const int t = v / SUB2, sub = v - t * SUB2;
   const int m_begin = t * NT2 + sub * NTS2, m_end = min(p.H, m_begin + NTS2);
+  load_rows(p, st, L, -1);
   for (int g0 = 0; g0 < p.B; g0 += RG) {
     const int nr = min(RG, p.B - g0);
-    stage_h(p, hs, p.h_shared, L, g0, nr, p.Is);
     Fc2Bf<RG, FULL> f;
     f.w = p.sd;
     f.K = p.Is;
@@ -805,21 +866,31 @@ __device__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.out_ld = p.H;
     f.row = L.slot + g0;
     const int groups = (m_end - m_begin + 31) / 32;  // 32 rows per block pass (4 waves x 8)
-    if (m_begin < m_end) run_passes<BfBuf<CPL2>>(f, groups * f.nseg);
+    const int P = m_begin < m_end ? groups * f.nseg : 0;
+    BfBuf<CPL2> ba, bb;
+    prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
+    if (g0 == 0) wg_wait_geq(p, ctrl_at(p, CTRL_SH1), (unsigned)p.n_s1);
+    stage_h(p, hs, p.h_shared, L, g0, nr, p.Is);
+    drive_passes(f, P, ba, bb);
   }
   fc2_ticket(p, st.U, L, t);
 }
 
 template <int RG, bool FULL>
-__device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int t) {
-  wg_wait_geq(p, (p.ctrl + ctrl_word(CTRL_FC1 + a)), (unsigned)p.T1);
-  load_rows(p, st, L, a);
+__device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v) {
+  const int t = v / SUBR, sub = v - t * SUBR;
+  const int m_begin = t * NT2 + sub * NTR2, m_end = min(p.H, m_begin + NTR2);
+  int expert;
+  if (p.B == 1) {
+    expert = wait_slot(p, L, a, (unsigned)p.T1);
+  } else {
+    load_rows(p, st, L, a);
+    expert = st.s_active[a];
+  }
   const int nrows_unit = L.nrows;
-  const uint8_t* blob = p.experts + (size_t)st.s_active[a] * p.blob_bytes;
-  const int m_begin = t * NT2, m_end = min(p.H, m_begin + NT2);
+  const uint8_t* blob = p.experts + (size_t)expert * p.blob_bytes;
   for (int g0 = 0; g0 < nrows_unit; g0 += RG) {
     const int nr = min(RG, nrows_unit - g0);
-    stage_h(p, hs, p.h_routed, L, g0, nr, p.I);
     Fc2Mx<RG, FULL> f;
     f.codes = blob + p.off[2];
     f.scales = blob + p.off[5];
@@ -836,9 +907,25 @@ __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.out_ld = p.H;
     f.slot = L.slot + g0;
     const int groups = (m_end - m_begin + 31) / 32;
-    run_passes<MxBuf<CPL2>>(f, groups * f.nseg);
+    const int P = m_begin < m_end ? groups * f.nseg : 0;
+    MxBuf<CPL2> ba, bb;
+    prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
+    if (g0 == 0 && p.B > 1) wg_wait_geq(p, ctrl_at(p, line_fc1(a)), (unsigned)p.T1);
+    stage_h(p, hs, p.h_routed, L, g0, nr, p.I);
+    drive_passes(f, P, ba, bb);
   }
   fc2_ticket(p, st.U, L, t);
+}
+
+// Next unit of the in-order queue (the first p.n_static units are handed out
+// by workgroup index; they never wait).
+__device__ __forceinline__ int pop_unit(const LayerParams& p, Lds& L) {
+  __syncthreads();
+  if (threadIdx.x == 0)
+    L.next = p.n_static +
+             (int)__hip_atomic_fetch_add(ctrl_at(p, CTRL_HEAD), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return L.next;
 }
 
 // ---- the kernel ------------------------------------------------------------------
@@ -853,54 +940,51 @@ __global__ __launch_bounds__(256, RG == 1 ? 3 : 2) void k_moe_layer(LayerParams 
   u32x4* hs = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(lds_raw) + p.lds_h_off);
   __shared__ Lds L;
   WgState st{false, false, 0, nullptr, nullptr, nullptr};
-  if (threadIdx.x == 0)
-    L.next = (int)__hip_atomic_fetch_add((p.ctrl + ctrl_word(CTRL_HEAD)), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  int u = L.next;
+  // First units (router and shared FC1 -- they wait on nothing) by workgroup
+  // index, so the launch ramp does not queue on the head counter.
+  int u = (int)blockIdx.x < p.n_static ? (int)blockIdx.x : pop_unit(p, L);
   for (;;) {
-    __syncthreads();
-    if (threadIdx.x == 0)  // fetch the next unit while this one runs
-      L.next = (int)__hip_atomic_fetch_add((p.ctrl + ctrl_word(CTRL_HEAD)), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int rel = u;
     if (rel < p.n_rt) {
-      router_unit<RG>(p, st, L, xs, rel);
-    } else if ((rel -= p.n_rt) < p.n_ro) {
-      routing_unit<TPL>(p, st, L, reinterpret_cast<int*>(lds_raw), rel);
-    } else if ((rel -= p.n_ro) < p.n_s1) {
+      router_unit<RG, TPL>(p, st, L, xs, rel);
+    } else if ((rel -= p.n_rt) < p.n_s1) {
       shared_fc1_unit<RG, FULL>(p, st, L, xs, rel);
     } else {
       rel -= p.n_s1;
       if (!st.route_seen) {
-        wg_wait_geq(p, (p.ctrl + ctrl_word(CTRL_READY)), 1u);
-        st.U = (int)ld_ctrl((p.ctrl + ctrl_word(CTRL_U)));
+        if (p.B == 1) {
+          st.U = p.k;  // one row: k distinct experts, one per slot
+        } else {
+          wg_wait_geq(p, ctrl_at(p, CTRL_READY), 1u);
+          st.U = (int)ld_ctrl(ctrl_at(p, CTRL_U));
+          cache_schedule(p, st, reinterpret_cast<int*>(reinterpret_cast<char*>(lds_raw) + p.lds_sched_off));
+        }
         st.route_seen = true;
-        cache_schedule(p, st, reinterpret_cast<int*>(reinterpret_cast<char*>(lds_raw) + p.lds_sched_off));
       }
       const int U = st.U;
       if (rel < U * p.T1) {
         routed_fc1_unit<RG, FULL>(p, st, L, xs, rel / p.T1, rel % p.T1);
       } else if ((rel -= U * p.T1) < p.n_s2) {
         shared_fc2_unit<RG, FULL>(p, st, L, hs, rel);
-      } else if ((rel -= p.n_s2) < U * p.T2) {
-        routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / p.T2, rel % p.T2);
+      } else if ((rel -= p.n_s2) < U * p.T2 * SUBR) {
+        routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / (p.T2 * SUBR), rel % (p.T2 * SUBR));
       } else {
         break;
       }
     }
-    __syncthreads();
-    u = L.next;
+    u = pop_unit(p, L);
   }
   // Exit: the last workgroup out clears the control block for the next call
   // (all other workgroups have made their final control-block access).
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add((p.ctrl + ctrl_word(CTRL_EXIT)), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned old = __hip_atomic_fetch_add(ctrl_at(p, CTRL_EXIT), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     L.flag = (old == gridDim.x - 1);
   }
   __syncthreads();
   if (L.flag) {
     for (int i = threadIdx.x; i < p.ctrl_words / CTRL_STRIDE; i += 256)
-      if (i != CTRL_ERR) st_coh(p.ctrl + ctrl_word(i), 0u);
+      if (i != CTRL_ERR) st_coh(ctrl_at(p, i), 0u);
   }
 }
 
@@ -923,8 +1007,8 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   int K2 = I > Is ? I : Is;
   s.hstride = ((K2 / 4 + 7) / 8) * 8;
   size_t x_bytes = (size_t)s.rg * s.xstride * 16;
-  // the routing unit reuses this region: top-k candidates (640 words), then
-  // the schedule's counts (2E) and slot ids (B*k)
+  // routing reuses this region: top-k candidates (640 words), then the
+  // schedule's counts (2E) and slot ids (B*k)
   size_t keys_bytes = 640 * 4, cnt_bytes = (size_t)(2 * E + B * k) * 4;
   size_t sched_bytes = keys_bytes > cnt_bytes ? keys_bytes : cnt_bytes;
   size_t xr = align256(x_bytes > sched_bytes ? x_bytes : sched_bytes);
@@ -937,7 +1021,7 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
 }
 
 template <int RG, bool FULL, int TPL>
-static hipError_t launch_t(const LayerParams& p, size_t lds, hipStream_t s) {
+static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
   auto kern = k_moe_layer<RG, FULL, TPL>;
   static thread_local int cached[2] = {-1, -1};  // (lds bytes, blocks per CU)
   int per_cu = 0;
@@ -948,7 +1032,9 @@ static hipError_t launch_t(const LayerParams& p, size_t lds, hipStream_t s) {
     cached[0] = (int)lds;
     cached[1] = per_cu;
   }
-  hipLaunchKernelGGL(kern, dim3(num_cus() * per_cu), dim3(256), lds, s, p);
+  const int grid = num_cus() * per_cu;
+  p.n_static = std::min(grid, p.n_rt + p.n_s1);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
@@ -988,7 +1074,7 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.xstride = sh.xstride;
   p.hstride = sh.hstride;
   p.n_rt = p.n_rt_e * ((a.B + sh.rg - 1) / sh.rg);
-  p.n_ro = a.B;
+  p.n_rb = (a.B + sh.rg - 1) / sh.rg;
   p.n_s1 = a.Is > 0 ? (a.Is + NTS1 - 1) / NTS1 : 0;
   p.T1 = (a.I + NT1 - 1) / NT1;
   p.T2 = (a.H + NT2 - 1) / NT2;

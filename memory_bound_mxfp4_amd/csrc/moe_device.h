@@ -265,9 +265,10 @@ __device__ __forceinline__ void router_dot(const uint16_t* __restrict__ wrow, in
 // Software-pipelined weight streams.  A wave walks a list of weight rows; LPR
 // lanes share a row (lane l takes 16-byte chunks l, l+LPR, ...), and a row is
 // cut into segments of CPL chunks per lane.  One "pass" = one segment of the
-// wave's current rows.  Pass p+1's loads are issued before pass p's math, so
-// every wave keeps CPL (or 2 x CPL) 16-byte loads in flight per lane.
-// The Traits type supplies load(), math() and finish() for a weight format.
+// wave's current rows.  The loads of the next two passes are in flight while
+// a pass's math runs, so every wave keeps CPL to 2 x CPL 16-byte loads in
+// flight per lane.  The Traits type supplies load() and math() (math of a
+// row's last segment also reduces and stores that row's outputs).
 // ---------------------------------------------------------------------------
 template <int CPL>
 struct MxBuf {  // MXFP4: 32 codes per chunk plus its E8M0 scale byte
@@ -282,18 +283,33 @@ struct BfBuf {  // bf16: 8 weights per chunk
 };
 
 // Drives P passes of a wave; Traits::load(buf, p) / Traits::math(buf, p).
+// prime_passes issues the loads of the first two passes; drive_passes then
+// alternates math of one pass with the loads of the pass after next, so two
+// passes are in flight.  A unit may do other work (wait, stage activations)
+// between the two while its first weights arrive.
+template <class Buf, class Traits>
+__device__ __forceinline__ void prime_passes(Traits& t, int P, Buf& a, Buf& b) {
+  if (P > 0) t.load(a, 0);
+  if (P > 1) t.load(b, 1);
+}
+
+template <class Buf, class Traits>
+__device__ __forceinline__ void drive_passes(Traits& t, int P, Buf& a, Buf& b) {
+  for (int p = 0; p < P; p += 2) {
+    t.math(a, p);
+    if (p + 2 < P) t.load(a, p + 2);
+    if (p + 1 < P) {
+      t.math(b, p + 1);
+      if (p + 3 < P) t.load(b, p + 3);
+    }
+  }
+}
+
 template <class Buf, class Traits>
 __device__ __forceinline__ void run_passes(Traits& t, int P) {
   Buf a, b;
-  if (P > 0) t.load(a, 0);
-  for (int p = 0; p < P; p += 2) {
-    if (p + 1 < P) t.load(b, p + 1);
-    t.math(a, p);
-    if (p + 1 < P) {
-      if (p + 2 < P) t.load(a, p + 2);
-      t.math(b, p + 1);
-    }
-  }
+  prime_passes(t, P, a, b);
+  drive_passes(t, P, a, b);
 }
 
 }  // namespace moe
