@@ -112,6 +112,79 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0):
     }
 
 
+KERNEL_SOURCES = ("layer.hip", "moe_device.h", "mx_common.h", "internal.h", "api.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_moe_layer_k3_b1_traffic.txt")
+CALIB_BYTES = 256 << 20  # plain device-to-device copy used to scale the HBM byte counters
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the layer kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "memory_bound_mxfp4_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def calibration_copy():
+    """One copy of CALIB_BYTES (read CALIB_BYTES, write CALIB_BYTES), outside any
+    timed region: a kernel of known traffic that counter runs scale by."""
+    import torch
+    a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def recorded_traffic():
+    """HBM bytes per k_moe_layer launch measured by counters (profiles file), or
+    None when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def pmc_summary(fetch_csv, write_csv, kernel="k_moe_layer"):
+    """Scaled HBM traffic of `kernel` from FETCH_SIZE and WRITE_SIZE counter CSVs
+    (rocprofv3 --pmc ... --output-format csv).  Each counter is scaled by the
+    ratio of the calibration copy's known bytes to what the counter read for it."""
+    import csv
+    import numpy as np
+
+    def per_kernel(path, counter):
+        vals, calib = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            name = r["Kernel_Name"]
+            if kernel in name:
+                vals.append(v)
+            elif "copyBuffer" in name:
+                calib.append(v)  # the runtime's copy kernel; the largest dispatch is the calibration copy
+        return vals, calib
+    f_vals, f_cal = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_vals, w_cal = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = CALIB_BYTES / (max(f_cal) * 1024)
+    w_scale = CALIB_BYTES / (max(w_cal) * 1024)
+    fetch = float(np.mean(f_vals)) * 1024 * f_scale
+    write = float(np.mean(w_vals)) * 1024 * w_scale
+    return {"fetch_kib_raw": float(np.mean(f_vals)), "write_kib_raw": float(np.mean(w_vals)),
+            "calib_fetch_kib": max(f_cal), "calib_write_kib": max(w_cal), "fetch_scale": f_scale,
+            "write_scale": w_scale, "fetch_bytes": int(fetch), "write_bytes": int(write),
+            "traffic_bytes_per_launch": int(fetch + write), "dispatches": len(f_vals),
+            "kernel_source_hash": kernel_source_hash()}
+
+
 def cpu_baseline(seed=0):
     """The oracle (single thread) on one K3-shaped batch-1 layer; expert regeneration excluded."""
     import numpy as np
@@ -145,7 +218,13 @@ def main():
     ap.add_argument("--variants", type=int, default=32, help="distinct input rows rotated across steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the batch-8 and batch-64 lines")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the scaled HBM traffic of k_moe_layer from two counter CSVs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        for k, v in pmc_summary(*args.pmc_summary).items():
+            print(f"{k} = {v}")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the layer fits one MI355X; "
               "this build has no multi-GPU path)", file=sys.stderr)
@@ -159,6 +238,7 @@ def main():
     cfg = CONFIGS["k3_b1"]
     print(f"[bench] generating {args.layers} K3-shaped layers in HBM", file=sys.stderr, flush=True)
     layers = [device_weights(cfg, 0, layer=l) for l in range(args.layers)]
+    calibration_copy()
     print("[bench] timing batch 1", file=sys.stderr, flush=True)
     main_r = run_config(cfg, layers, args.steps, args.warmup, args.variants)
     extra = {}
@@ -200,7 +280,7 @@ def main():
         "kernels_per_layer": len(main_r["kernel_us"]),
         "kernel_us": {k: round(v, 2) for k, v in main_r["kernel_us"].items()},
         "roofline": {"kernel": "k_moe_layer", "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": recorded_traffic(),
                      "algorithmic_bytes_per_launch": int(fc1_bytes), "avg_launch_us": round(fc1_us, 2)},
         "cpu_baseline": cpu,
         "extra_configs": extra,
