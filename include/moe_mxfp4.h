@@ -80,6 +80,10 @@ typedef enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 } moe_dtype;
 #define MOE_MAX_TOPK 64
 #define MOE_MAX_EXPERTS 4096
 
+/* Layout of the experts buffer (moe_layer_weights.expert_layout). */
+#define MOE_EXPERTS_CANONICAL 0 /* the blob layout described above             */
+#define MOE_EXPERTS_PACKED 1    /* rewritten by moe_pack_experts (see below)    */
+
 /*
  * One layer's weights: a host struct of device pointers.
  *   hidden H, inter I (routed expert intermediate), num_experts E, top_k k,
@@ -90,7 +94,9 @@ typedef enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 } moe_dtype;
  *                NULL for none
  *   shared_gate, shared_up  bf16 [Is][H];  shared_down  bf16 [H][Is];
  *                all three NULL iff Is == 0
- *   experts      E blobs of moe_expert_bytes(H, I) bytes (layout above)
+ *   experts      E blobs of moe_expert_bytes(H, I) bytes
+ *   expert_layout  MOE_EXPERTS_CANONICAL or MOE_EXPERTS_PACKED: which layout
+ *                the experts buffer holds (moe_decode_layer needs PACKED)
  * bf16 tensors are raw bfloat16 bit patterns (uint16_t).
  */
 typedef struct {
@@ -101,6 +107,7 @@ typedef struct {
   const uint16_t* shared_up;
   const uint16_t* shared_down;
   const uint8_t* experts;
+  int32_t expert_layout;
 } moe_layer_weights;
 
 /* Bytes of one expert blob (17,547,264 at H 7168, I 1536); 0 if H or I is
@@ -111,6 +118,36 @@ size_t moe_expert_bytes(int hidden, int inter);
  * Returns MOE_ERR_INVALID_ARGUMENT for the same shape errors as
  * moe_decode_layer. */
 moe_status moe_workspace_size(const moe_layer_weights* w, int batch, size_t* bytes);
+
+/*
+ * moe_pack_experts / moe_unpack_experts -- rewrite experts [0, num_experts)
+ * of an experts buffer IN PLACE from the canonical blob layout into the
+ * packed layout moe_decode_layer streams, or back.  Done once, when the
+ * weights are loaded; not part of a decode step.  Each blob keeps its size
+ * (moe_expert_bytes) and position; the rewrite is an exact byte permutation.
+ *
+ * Packed layout.  Each MXFP4 matrix [N][K] of a blob is cut into tiles of 16
+ * rows x 16 scale blocks (16 x 512 elements; the last tile of a row group
+ * holds the remaining K/32 mod 16 blocks).  A tile of SC blocks holds its
+ * codes as [SC][16 rows] x 16 bytes followed by its scales as [16 rows][SC]
+ * bytes; a row group's tiles are consecutive.  The blob holds, for every
+ * 16-row group of the gate/up rows and every segment along H, the gate tile
+ * then the up tile; then the down tiles (16-row groups of H, segments along
+ * I); then zero padding up to moe_expert_bytes.  So a wave of 64 lanes reads
+ * 16 rows x 128 elements of codes as one contiguous kilobyte, with the tile's
+ * scales right behind it.
+ *
+ *   experts  device buffer of num_experts * moe_expert_bytes(H, I) bytes,
+ *            256-byte aligned
+ *   scratch  device buffer of >= moe_expert_bytes(H, I) bytes, not
+ *            overlapping experts (one expert is staged through it at a time)
+ * Enqueued on `stream`; the buffer must not be used by other work until the
+ * stream has passed the call.
+ */
+moe_status moe_pack_experts(uint8_t* experts, int num_experts, int hidden, int inter, void* scratch,
+                            size_t scratch_bytes, void* stream);
+moe_status moe_unpack_experts(uint8_t* experts, int num_experts, int hidden, int inter, void* scratch,
+                              size_t scratch_bytes, void* stream);
 
 /*
  * router_topk -- router GEMV, top-k selection and renormalised gates.
@@ -142,18 +179,21 @@ moe_status expert_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int n,
 
 /*
  * moe_workspace_init -- clear a workspace before its first use.
- * The first bytes of a layer workspace are a control block of counters that
- * moe_decode_layer's single persistent kernel synchronises on.  It must be
- * zero when a call starts; every call leaves it zero again when it ends, so
- * a workspace needs this (or any zero fill of the whole buffer) once after
- * allocation, and again only after a call that did not complete (a device
- * fault).  Enqueued on `stream`.  ws 256-byte aligned, ws_bytes a multiple
- * of 16.
+ * The first bytes of a layer workspace are a control block that
+ * moe_decode_layer's single persistent kernel synchronises through: a
+ * work-queue counter (zero between calls) and a call epoch that every call
+ * advances.  Data that workgroups of one call hand to each other is tagged
+ * with that call's epoch, so stale data of an earlier call is never taken
+ * for the current call's.  A workspace therefore needs this (or any zero
+ * fill of the whole buffer) once after allocation, and again after a call
+ * that did not complete (a device fault).  Enqueued on `stream`.  ws
+ * 256-byte aligned, ws_bytes a multiple of 16.
  * The uint32 at byte offset MOE_WS_STATUS_OFFSET of the workspace is a sticky
  * status word: nonzero means a synchronisation wait inside a call timed out
- * (about a second), which only happens if the control block was not zero at
- * the start of a call; the outputs of such a call are not valid.  It is
- * cleared by moe_workspace_init.
+ * (about a second), which only happens if the workspace was not initialised
+ * or the launch could not keep all of its workgroups resident; the outputs
+ * of such a call are not valid.  It is cleared by moe_workspace_init.
+ * Tags repeat after 2^32 calls on one workspace.
  */
 #define MOE_WS_STATUS_OFFSET 28
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
@@ -164,6 +204,8 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   residual   fp32 [batch][hidden], read and overwritten with
  *              residual + shared + sum_j gate_j * expert_j; must not alias x
  *   topk_idx   out int32 [batch][top_k]; topk_gate out fp32 [batch][top_k]
+ *   w          weights with expert_layout == MOE_EXPERTS_PACKED (a canonical
+ *              experts buffer returns MOE_ERR_UNSUPPORTED: pack it once first)
  *   ws         workspace of >= moe_workspace_size(w, batch) bytes, 256-byte
  *              aligned, owned by the caller, cleared once by
  *              moe_workspace_init; calls that share a workspace must be

@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_DTYPE_BF16, MOE_DTYPE_F32 = 0, 1
+MOE_EXPERTS_CANONICAL, MOE_EXPERTS_PACKED = 0, 1
 MAX_BATCH = 64
 
 # Symbols the C header declares (checked by tests/test_abi.py).
 EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size", "router_topk",
            "expert_gemv_mxfp4", "moe_decode_layer", "moe_decode_layer_kernel_count",
-           "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16",
-           "moe_status_string")
+           "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "moe_pack_experts",
+           "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -38,7 +39,7 @@ class LayerWeightsC(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("shared_gate", ctypes.c_void_p), ("shared_up", ctypes.c_void_p),
-                ("shared_down", ctypes.c_void_p), ("experts", ctypes.c_void_p)]
+                ("shared_down", ctypes.c_void_p), ("experts", ctypes.c_void_p), ("expert_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -65,6 +66,8 @@ def load():
         "moe_decode_layer_kernel_name": (ctypes.c_char_p, [I]),
         "moe_decode_layer_timed": (I, [P, P, P, I, P, P, P, Z, P, P, I]),
         "moe_workspace_init": (I, [P, Z, P]),
+        "moe_pack_experts": (I, [P, I, I, I, P, Z, P]),
+        "moe_unpack_experts": (I, [P, I, I, I, P, Z, P]),
         "rmsnorm_bf16": (I, [P, I, I, F, P, P]),
         "dense_gemv_bf16": (I, [P, I, I, P, I, P, P]),
         "residual_add_bf16": (I, [P, P, I, I, P]),
@@ -116,6 +119,7 @@ class LayerWeights:
     shared_gate: Optional[object] = None
     shared_up: Optional[object] = None
     shared_down: Optional[object] = None
+    expert_layout: int = MOE_EXPERTS_CANONICAL
 
     def __setattr__(self, name, value):
         object.__setattr__(self, name, value)
@@ -128,9 +132,37 @@ class LayerWeights:
             return cs
         cs = LayerWeightsC(self.hidden, self.inter, self.num_experts, self.top_k, self.shared_inter,
                              _ptr(self.router_w), _ptr(self.router_bias), _ptr(self.shared_gate),
-                             _ptr(self.shared_up), _ptr(self.shared_down), _ptr(self.experts))
+                             _ptr(self.shared_up), _ptr(self.shared_down), _ptr(self.experts), self.expert_layout)
         object.__setattr__(self, "_cs", cs)
         return cs
+
+
+def _pack(experts, num_experts: int, hidden: int, inter: int, to_packed: bool, scratch=None, stream=None):
+    import torch
+    nb = expert_bytes(hidden, inter)
+    scratch = torch.empty(nb, dtype=torch.uint8, device=experts.device) if scratch is None else scratch
+    f = load().moe_pack_experts if to_packed else load().moe_unpack_experts
+    _check(f(_ptr(experts), num_experts, hidden, inter, _ptr(scratch), scratch.numel(), _stream(stream)),
+           "moe_pack_experts" if to_packed else "moe_unpack_experts")
+    return experts
+
+
+def pack_experts(experts, num_experts: int, hidden: int, inter: int, scratch=None, stream=None):
+    """Rewrite canonical expert blobs in place into the packed layout (moe_pack_experts)."""
+    return _pack(experts, num_experts, hidden, inter, True, scratch, stream)
+
+
+def unpack_experts(experts, num_experts: int, hidden: int, inter: int, scratch=None, stream=None):
+    """Inverse of pack_experts (moe_unpack_experts)."""
+    return _pack(experts, num_experts, hidden, inter, False, scratch, stream)
+
+
+def pack_layer(w: LayerWeights, stream=None) -> LayerWeights:
+    """Pack a layer's experts in place (once, at load time) and mark them packed."""
+    if w.expert_layout != MOE_EXPERTS_PACKED:
+        pack_experts(w.experts, w.num_experts, w.hidden, w.inter, stream=stream)
+        w.expert_layout = MOE_EXPERTS_PACKED
+    return w
 
 
 def workspace_size(w: LayerWeights, batch: int) -> int:

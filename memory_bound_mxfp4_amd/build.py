@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SO = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["api.hip", "router.hip", "experts.hip", "dense.hip", "layer.hip"]
+SOURCES = ["api.hip", "router.hip", "experts.hip", "dense.hip", "pack.hip", "layer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -34,17 +34,17 @@ Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B) {
   const size_t slots = (size_t)B * k;
   const size_t umax = slots < (size_t)E ? slots : (size_t)E;
   w.umax = (int)umax;
-  w.ctrl_words = ctrl_lines((int)umax, layer_tiles_fc2(H)) * CTRL_STRIDE;
-  w.ctrl = reinterpret_cast<unsigned*>(take(sizeof(unsigned) * (size_t)w.ctrl_words));
-  w.logits = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * E));
-  w.sched.n_active = reinterpret_cast<int*>(take(sizeof(int)));
+  w.ctrl = reinterpret_cast<unsigned*>(take(sizeof(unsigned) * CTRL_WORDS));
+  w.logits_p = reinterpret_cast<uint64_t*>(take(8 * (size_t)B * E));
+  w.idx_p = reinterpret_cast<uint64_t*>(take(8 * slots));
+  w.gate_p = reinterpret_cast<uint64_t*>(take(8 * slots));
   w.sched.active = reinterpret_cast<int*>(take(sizeof(int) * umax));
   w.sched.row_off = reinterpret_cast<int*>(take(sizeof(int) * (umax + 1)));
   w.sched.rows = reinterpret_cast<int*>(take(sizeof(int) * slots));
-  w.h_shared = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * (Is > 0 ? Is : 1)));
-  w.h_routed = reinterpret_cast<float*>(take(sizeof(float) * slots * I));
-  w.o_shared = reinterpret_cast<float*>(take(sizeof(float) * (size_t)B * H));
-  w.o_routed = reinterpret_cast<float*>(take(sizeof(float) * slots * H));
+  w.hs_p = reinterpret_cast<uint64_t*>(take(8 * (size_t)B * (Is > 0 ? Is : 1)));
+  w.hr_p = reinterpret_cast<uint64_t*>(take(8 * slots * I));
+  w.os_p = reinterpret_cast<uint64_t*>(take(8 * (size_t)B * H));
+  w.or_p = reinterpret_cast<uint64_t*>(take(8 * slots * H));
   w.bytes = o;
   return w;
 }
@@ -77,6 +77,8 @@ static moe_status check_layer(const moe_layer_weights* w, int batch) {
   if (!w->router_w || !w->experts) return MOE_ERR_INVALID_ARGUMENT;
   if (Is > 0 && (!w->shared_gate || !w->shared_up || !w->shared_down)) return MOE_ERR_INVALID_ARGUMENT;
   if (Is == 0 && (w->shared_gate || w->shared_up || w->shared_down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->expert_layout != MOE_EXPERTS_CANONICAL && w->expert_layout != MOE_EXPERTS_PACKED)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(w->router_w, 16) || !aligned(w->experts, 256) || (w->router_bias && !aligned(w->router_bias, 4)))
     return MOE_ERR_INVALID_ARGUMENT;
   if (Is > 0 && (!aligned(w->shared_gate, 16) || !aligned(w->shared_up, 16) || !aligned(w->shared_down, 16)))
@@ -153,6 +155,7 @@ static moe_status run_layer(const moe_layer_weights* w, const uint16_t* x, float
   if (st != MOE_OK) return st;
   if (!x || !residual || !topk_idx || !topk_gate || !ws) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(ws, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->expert_layout != MOE_EXPERTS_PACKED) return MOE_ERR_UNSUPPORTED;
   const int H = w->hidden, I = w->inter, E = w->num_experts, k = w->top_k, Is = w->shared_inter;
   Workspace wsl = ws_layout(ws, H, I, E, k, Is, batch);
   if (ws_bytes < wsl.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -203,6 +206,30 @@ moe_status moe_decode_layer_timed(const moe_layer_weights* w, const uint16_t* x,
     if (!events[i]) return MOE_ERR_INVALID_ARGUMENT;
   return run_layer(w, x, residual, batch, topk_idx, topk_gate, ws, ws_bytes, static_cast<hipStream_t>(stream),
                    events);
+}
+
+static moe_status pack_common(uint8_t* experts, int E, int H, int I, void* scratch, size_t scratch_bytes,
+                              void* stream, bool to_packed) {
+  if (!experts || !scratch || E < 1 || H <= 0 || I <= 0 || H % 32 || I % 32) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(experts, 256) || !aligned(scratch, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t nb = blob_layout(H, I).bytes;
+  if (scratch_bytes < nb) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const uint8_t* sc = static_cast<const uint8_t*>(scratch);
+  if (sc < experts + (size_t)E * nb && experts < sc + nb) return MOE_ERR_INVALID_ARGUMENT;  // overlap
+  if (launch_pack_experts(experts, E, H, I, static_cast<uint8_t*>(scratch), to_packed,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_pack_experts(uint8_t* experts, int num_experts, int hidden, int inter, void* scratch,
+                            size_t scratch_bytes, void* stream) {
+  return pack_common(experts, num_experts, hidden, inter, scratch, scratch_bytes, stream, true);
+}
+
+moe_status moe_unpack_experts(uint8_t* experts, int num_experts, int hidden, int inter, void* scratch,
+                              size_t scratch_bytes, void* stream) {
+  return pack_common(experts, num_experts, hidden, inter, scratch, scratch_bytes, stream, false);
 }
 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {

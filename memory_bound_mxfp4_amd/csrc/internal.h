@@ -21,54 +21,44 @@ struct BlobLayout {
 BlobLayout blob_layout(int H, int I);
 
 // Expert-gathered schedule built on the device from the top-k indices.
-//   n_active          number U of distinct experts any row selected
-//   active[U]         their ids, ascending
+//   active[U]         the U distinct experts any row selected, ascending
 //   row_off[U+1]      rows of active expert a are rows[row_off[a] .. row_off[a+1])
 //   rows[B*k]         slot ids s = b * k + j
 struct Sched {
-  int* n_active;
   int* active;
   int* row_off;
   int* rows;
 };
 
-// Control block at the start of the workspace: counters of uint32, each on a
-// 128-byte line of its own (counter i at word CTRL_STRIDE * i), so that polls
-// of different counters never share a cache line.  Zeroed once by
-// moe_workspace_init; every layer call leaves it zeroed again, except the
-// sticky error word.
+// Control block at the start of the workspace: uint32 words, each counter on
+// a 128-byte line of its own (line i starts at word CTRL_STRIDE * i) so that
+// polls of different counters never share a cache line.
+//   line 0, word 0   work-queue head                (zero between calls)
+//   line 0, word 7   sticky error word (byte offset MOE_WS_STATUS_OFFSET)
+//   line 1           workgroups that have exited    (zero between calls)
+//   line 2           call epoch: bumped by the last workgroup of every call
+//   line 3           schedule-ready word pair (batch > 1): U | tag << 32
+// Data handed between workgroups inside a call travels as 8-byte pairs
+// (32-bit value | 32-bit tag << 32), tag = epoch + 1 of the call, written and
+// read with single 8-byte coherent accesses: a consumer polls the data itself
+// until every pair carries its call's tag, so no producer ever has to drain
+// its stores and bump a counter.
 constexpr int CTRL_STRIDE = 32;
-enum {
-  CTRL_HEAD = 0,     // work-queue head
-  CTRL_ROUTER = 1,   // (unused)
-  CTRL_ROUTING = 2,  // rows routed (batch > 1)
-  CTRL_READY = 3,    // schedule published (0/1, batch > 1)
-  CTRL_U = 4,        // number of distinct experts (batch > 1)
-  CTRL_SH1 = 5,      // shared FC1 units done
-  CTRL_EXIT = 6,     // workgroups that have exited
-  CTRL_ERR = 7,      // sticky: a bounded wait expired (byte offset 28: in the first line)
-  CTRL_FC1 = 8       // first of the per-launch arrays below
-};
-// Counter lines after CTRL_FC1: [umax] routed FC1 units done per active expert
-// (per slot at batch 1), [T2] FC2 tile tickets, [MOE_MAX_BATCH] router
-// row-block tickets, [MOE_MAX_TOPK] published expert + 1 of each slot (batch 1).
-__host__ __device__ constexpr int ctrl_lines(int umax, int T2) {
-  return CTRL_FC1 + umax + T2 + MOE_MAX_BATCH + MOE_MAX_TOPK;
-}
-// Word index of counter i (the error word stays at word 7 of the first line).
-__host__ __device__ constexpr int ctrl_word(int i) { return i == CTRL_ERR ? CTRL_ERR : i * CTRL_STRIDE; }
+constexpr int CTRL_HEAD = 0, CTRL_ERR = 7, CTRL_EXIT = 1 * CTRL_STRIDE, CTRL_EPOCH = 2 * CTRL_STRIDE,
+              CTRL_READY = 3 * CTRL_STRIDE, CTRL_WORDS = 4 * CTRL_STRIDE;
 
 // Workspace of moe_decode_layer.
 struct Workspace {
   unsigned* ctrl;
-  int ctrl_words;
   int umax;
-  float* logits;    // [B][E]
-  Sched sched;
-  float* h_shared;  // [B][Is]
-  float* h_routed;  // [B*k][I]
-  float* o_shared;  // [B][H]
-  float* o_routed;  // [B*k][H]
+  uint64_t* logits_p;  // [B][E]      router logits
+  uint64_t* idx_p;     // [B*k]       expert of slot s = b*k + j
+  uint64_t* gate_p;    // [B*k]       gate of slot s
+  Sched sched;         // batch > 1: expert-gathered schedule (plain ints, published by READY)
+  uint64_t* hs_p;      // [B][Is]     shared-expert SwiGLU output
+  uint64_t* hr_p;      // [B*k][I]    routed SwiGLU output, by slot
+  uint64_t* os_p;      // [B][H]      shared-expert output
+  uint64_t* or_p;      // [B*k][H]    routed expert outputs, by slot
   size_t bytes;
 };
 Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B);
@@ -89,8 +79,9 @@ struct LayerArgs {
   float* residual;
 };
 hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* wr, int32_t* idx, hipStream_t s);
-int layer_tiles_fc2(int H);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_pack_experts(uint8_t* experts, int E, int H, int I, uint8_t* scratch, bool to_packed,
+                               hipStream_t s);
 
 hipError_t launch_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int N, int K, const void* x, bool x_f32,
                              int B, float* y, hipStream_t s);

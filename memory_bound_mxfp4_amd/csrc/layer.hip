@@ -8,29 +8,33 @@
 // and a tail that folds the down-projection reduction into what follows.
 // On one MI355X the same goal is met with a single launch:
 //
-//   * workgroups pop "units" from an in-order device queue (one atomic);
+//   * workgroups take "units" from an in-order device queue (one atomic,
+//     issued one unit ahead so its latency hides behind the current unit);
 //   * unit kinds, in queue order:
-//       router GEMV (4 experts x a block of rows)      -> logits
-//       routing (top-k + gates of one row; the last one builds the
-//                expert-gathered schedule)             -> idx, gate, schedule
-//       shared-expert FC1+SwiGLU (tile of Is rows)     -> h_shared
-//       routed FC1+SwiGLU (expert, tile of I rows)     -> h_routed
-//       shared-expert FC2 (64 rows of H)               -> o_shared
-//       routed FC2 (expert, tile of 256 rows of H)     -> o_routed, and the
-//                last contribution to a 256-row tile folds residual +=
-//                o_shared + sum_j gate_j o_j for that tile (fixed j order);
-//   * a unit waits only on units earlier in the queue (on a counter their
-//     completions bump), so the smallest unfinished unit can always run: no
-//     residency assumption, no deadlock; every wait is bounded and sets a
-//     sticky error word instead of hanging;
-//   * data handed between workgroups moves with coherent (sc1) loads and
-//     stores, so no L2 write-back or invalidate is ever issued -- on MI355X
-//     those serialise device-wide at a few per microsecond; coherent loads
-//     travel to the device coherence point, so they are always issued in
-//     batches (one round trip per batch);
+//       router GEMV (2 experts x a block of rows)          -> logits
+//       routing (top-k + gates of one row)                 -> idx, gate
+//       schedule (batch > 1: expert-gathered row lists)    -> schedule
+//       shared-expert FC1+SwiGLU (tile of Is rows)         -> shared h
+//       routed FC1+SwiGLU (expert, 16 rows of I)           -> routed h
+//       shared-expert FC2 (tile of H rows)                 -> shared output
+//       routed FC2 (expert, 128 rows of H)                 -> routed outputs
+//       combine (row, 256 rows of H): residual += shared + sum_j gate_j o_j
+//                (fixed j order, so the result is deterministic);
+//   * a unit only ever waits on data written by units earlier in the queue,
+//     so the smallest unfinished unit can always run: no residency
+//     assumption, no deadlock; every wait is bounded and sets a sticky error
+//     word instead of hanging;
+//   * data handed between workgroups travels as 8-byte (value, tag) pairs
+//     written and read with single coherent accesses (the tag identifies the
+//     call), and the consumer polls the data itself.  A producer therefore
+//     never drains its stores or bumps a completion counter: under a
+//     saturated HBM each such handshake is a multi-microsecond round trip,
+//     and there would be several per unit.  Coherent accesses are performed
+//     at the device coherence point, so no L2 write-back or invalidate (which
+//     serialise device-wide) is ever issued;
 //   * the router and the shared expert need no routing, so they stream while
-//     top-k runs, hiding its latency; routed FC2 of one expert overlaps FC1 of
-//     the next; the combine happens in the FC2 tail.
+//     top-k runs, hiding its latency; routed FC2 of one expert overlaps FC1
+//     of the next.
 //
 // Weight streams are branch-free: every lane issues all of a pass's 16-byte
 // loads (clamped to the row), and chunks past the row end are masked to zero
@@ -38,8 +42,8 @@
 // flight instead of waiting load by load.
 //
 // The control block at the start of the workspace is zeroed once by
-// moe_workspace_init and left zeroed by every call (the last workgroup to
-// exit clears it), so a call needs no separate clearing launch.
+// moe_workspace_init; the last workgroup of every call resets the queue and
+// advances the call epoch (whose value + 1 is the next call's tag).
 #include "internal.h"
 #include "moe_device.h"
 
@@ -47,13 +51,11 @@
 
 namespace moe {
 
-constexpr int NT1 = 16;   // routed FC1 rows (of I) per unit: 16 x 2 x 3.8 KB at H 7168
+constexpr int NT1 = 16;   // routed FC1 rows (of I) per unit: one packed row group, 16 x 2 x 3.8 KB at H 7168
 constexpr int NTS1 = 4;   // shared FC1 rows (of Is) per unit: 4 x 2 x 14 KB of bf16
-constexpr int NT2 = 256;  // FC2 tile (rows of H): the combine's granularity
+constexpr int NT2 = 256;  // combine tile (rows of H)
 constexpr int NTS2 = 32;  // shared FC2 rows per unit
-constexpr int NTR2 = 128; // routed FC2 rows per unit
-constexpr int SUB2 = NT2 / NTS2;  // shared FC2 units per tile
-constexpr int SUBR = NT2 / NTR2;  // routed FC2 units per tile and expert
+constexpr int NTR2 = 128; // routed FC2 rows per unit: 8 packed row groups
 constexpr int CPL1 = 7;   // FC1: 16-byte chunks per lane per pass (half-wave rows)
 constexpr int CPL2 = 6;   // FC2: 16-byte chunks per lane per pass (8 lanes per row)
 constexpr int MAX_ROWS = MOE_MAX_BATCH;    // activation rows one expert can have
@@ -71,85 +73,38 @@ struct LayerParams {
   float* residual;
   int32_t* idx;
   float* gate;
-  float* logits;
+  uint64_t* logits_p;
+  uint64_t* idx_p;
+  uint64_t* gate_p;
   int* active;
   int* row_off;
   int* rows;
-  float* h_shared;
-  float* h_routed;
-  float* o_shared;
-  float* o_routed;
+  uint64_t* hs_p;
+  uint64_t* hr_p;
+  uint64_t* os_p;
+  uint64_t* or_p;
   unsigned* ctrl;
   int umax;
-  int n_rt_e;  // router expert pairs (2 experts per unit, 2 waves per expert)
-  int n_rt;    // router units = n_rt_e * row blocks
-  int n_rb;    // router row blocks
+  int n_rt_e;    // router expert pairs (2 experts per unit, 2 waves per expert)
+  int n_rb;      // router row blocks
+  int n_rt;      // router units = n_rt_e * n_rb
+  int n_ro;      // routing units (one per row)
+  int n_sch;     // schedule units (batch > 1: 1)
+  int n_s1;      // shared FC1 units
+  int T1;        // routed FC1 tiles per expert
+  int n_s2;      // shared FC2 units
+  int n_r2;      // routed FC2 units per expert
+  int n_tile;    // combine tiles over H
+  int n_front;   // units before the routed ones (router .. shared FC1)
   int n_static;  // units 0 .. n_static-1 go to workgroups 0 .. n_static-1
-  int n_s1;    // shared FC1 units
-  int T1;      // routed FC1 tiles per expert
-  int T2;      // FC2 tiles over H (the combine's granularity)
-  int n_s2;    // shared FC2 units (SUB2 per tile)
-  int ctrl_words;
   int xstride;        // LDS x row stride, 16-byte granules (multiple of 8)
   int hstride;        // LDS h row stride, 16-byte granules (multiple of 8)
   int lds_h_off;      // byte offset of the h staging region in dynamic LDS
   int lds_sched_off;  // byte offset of the schedule copy in dynamic LDS
 };
 
-// ---- synchronisation helpers (the whole workgroup calls them) ---------------
-//
-// Producers write shared data with coherent stores (st_coh), wait until all
-// of their memory operations have completed (s_waitcnt 0), meet at a barrier,
-// and one thread bumps a counter with an agent-scope atomic.  Consumers poll
-// the counter (agent-scope atomic loads), meet at a barrier, and read the data
-// with coherent loads (ld_coh).  Compiler signal fences keep the accesses on
-// their side of the handshake.  There is no L2 write-back or invalidate.
-
-__device__ __forceinline__ unsigned ld_ctrl(const unsigned* a) {
-  return __hip_atomic_load(const_cast<unsigned*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until *a >= target.  Polls back off exponentially (to ~1 us between
-// polls) so that hundreds of waiting workgroups do not flood the coherence
-// point that every coherent access goes through.  Gives up after about a
-// second and sets the sticky error word (the unit then computes on whatever
-// it finds).
-__device__ __forceinline__ void wg_wait_geq(const LayerParams& p, const unsigned* a, unsigned target) {
-  if (threadIdx.x == 0) {
-    unsigned it = 0, nap = 1;
-    while (ld_ctrl(a) < target) {
-      if (nap <= 1) __builtin_amdgcn_s_sleep(1);
-      else if (nap <= 2) __builtin_amdgcn_s_sleep(2);
-      else if (nap <= 4) __builtin_amdgcn_s_sleep(4);
-      else if (nap <= 8) __builtin_amdgcn_s_sleep(8);
-      else if (nap <= 16) __builtin_amdgcn_s_sleep(16);
-      else __builtin_amdgcn_s_sleep(32);
-      nap = nap < 32 ? 2 * nap : 32;
-      if (++it >= SPIN_LIMIT) {
-        __hip_atomic_fetch_or((p.ctrl + ctrl_word(CTRL_ERR)), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// All of this workgroup's coherent stores complete, then *a += 1.
-// Returns the old value to thread 0 (others get 0).
-__device__ __forceinline__ unsigned wg_signal_add(unsigned* a) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  unsigned old = 0;
-  if (threadIdx.x == 0) old = __hip_atomic_fetch_add(a, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return old;
-}
-
-__device__ __forceinline__ uint64_t ld_coh64(const float* p) {
-  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void set_error(const LayerParams& p) {
+  __hip_atomic_fetch_or(p.ctrl + CTRL_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- per-workgroup state ------------------------------------------------------
@@ -157,51 +112,94 @@ __device__ __forceinline__ uint64_t ld_coh64(const float* p) {
 struct Lds {  // static LDS of the kernel
   int next;        // next unit index
   int flag;        // "this workgroup is the last arriver"
+  unsigned tag;    // this call's pair tag
+  int U;           // distinct experts (once known)
   int wtot[8];     // scan scratch
   int nrows;       // rows of the current unit
-  int expert;      // expert of the current routed unit (batch 1)
   double part[4][4];  // router: partial sums of the second half-row waves [wave][row]
+  float gates[MOE_MAX_TOPK];  // combine: gates of the current row
+  float red[4][4][16][2];     // routed FC1: per-wave partial sums [wave][row][tile row][gate/up]
   int slot[MAX_ROWS];  // slot ids (routed) or batch rows (shared) of the current unit
 };
 
 struct WgState {
   bool x_cached;    // batch 1: x row 0 already in LDS
-  bool route_seen;  // this workgroup has seen the routing published
+  bool route_seen;  // this workgroup holds the schedule in LDS
   int U;
+  uint32_t tag;
   const int* s_active;   // LDS copy of the schedule (valid once route_seen)
   const int* s_row_off;
   const int* s_rows;
 };
 
-// Copy the published schedule into this workgroup's LDS (one batch of
-// coherent loads), so routed units read it without a round trip.
-__device__ __forceinline__ void cache_schedule(const LayerParams& p, WgState& st, int* sc) {
-  const int U = st.U, nslots = p.B * p.k;
+// Bounded poll of one control word until it has `tag` in its high half
+// (thread 0 only); returns the low half.
+__device__ __forceinline__ uint32_t poll_ready(const LayerParams& p, uint32_t tag) {
+  const uint64_t* a = reinterpret_cast<const uint64_t*>(p.ctrl + CTRL_READY);
+  uint64_t v;
+  for (unsigned it = 0;; ++it) {
+    v = ld_pair(a);
+    if (pair_has(v, tag)) break;
+    if (it >= SPIN_LIMIT || ((it & 255) == 255 && ld_coh(p.ctrl + CTRL_ERR) != 0u)) {
+      set_error(p);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return (uint32_t)v;
+}
+
+// The schedule into this workgroup's LDS.  Batch 1: one row, so slot j is
+// "active expert" j with row list {j}; its expert comes from the routing
+// pairs.  Batch > 1: wait for the schedule unit's ready word, then copy the
+// published schedule (one batch of coherent loads).
+__device__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* sc) {
   int* a = sc;
   int* ro = sc + p.umax;
   int* rw = ro + p.umax + 1;
-  const int total = U + (U + 1) + nslots;
-  for (int base = threadIdx.x; base < total; base += 256 * 8) {
-    int v[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int i = min(base + 256 * t, total - 1);
-      v[t] = i < U ? ld_coh(p.active + i) : (i < 2 * U + 1 ? ld_coh(p.row_off + (i - U)) : ld_coh(p.rows + (i - 2 * U - 1)));
+  if (p.B == 1) {
+    if (threadIdx.x < p.k) {
+      uint64_t v[1];
+      const int j = threadIdx.x;
+      if (!poll_pairs<1>(p.idx_p, 1, [&](int) { return j; }, st.tag, v, SPIN_LIMIT, p.ctrl + CTRL_ERR)) set_error(p);
+      a[j] = (int)min((uint32_t)v[0], (uint32_t)p.E - 1u);
+      ro[j] = j;
+      rw[j] = j;
     }
+    if (threadIdx.x == 0) {
+      ro[p.k] = p.k;
+      L.U = p.k;
+    }
+  } else {
+    if (threadIdx.x == 0) L.U = (int)min(poll_ready(p, st.tag), (uint32_t)p.umax);
+    __syncthreads();
+    const int U = L.U, nslots = p.B * p.k;
+    const int total = U + (U + 1) + nslots;
+    for (int base = threadIdx.x; base < total; base += 256 * 8) {
+      int v[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int i = base + 256 * t;
-      if (i < total) {
-        if (i < U) a[i] = v[t];
-        else if (i < 2 * U + 1) ro[i - U] = v[t];
-        else rw[i - 2 * U - 1] = v[t];
+      for (int t = 0; t < 8; ++t) {
+        const int i = min(base + 256 * t, total - 1);
+        v[t] = i < U ? ld_coh(p.active + i)
+                     : (i < 2 * U + 1 ? ld_coh(p.row_off + (i - U)) : ld_coh(p.rows + (i - 2 * U - 1)));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int i = base + 256 * t;
+        if (i < total) {
+          if (i < U) a[i] = v[t];
+          else if (i < 2 * U + 1) ro[i - U] = v[t];
+          else rw[i - 2 * U - 1] = v[t];
+        }
       }
     }
   }
   __syncthreads();
+  st.U = L.U;
   st.s_active = a;
   st.s_row_off = ro;
   st.s_rows = rw;
+  st.route_seen = true;
 }
 
 // Row list of the current unit: batch rows 0..B-1 for the shared expert,
@@ -235,31 +233,34 @@ __device__ __forceinline__ void stage_x(const LayerParams& p, WgState& st, const
   st.x_cached = (p.B == 1);
 }
 
-// h rows (fp32 intermediate written earlier in this launch) of rows [g0,
-// g0+nr), row r taken from src[slot(r)]; coherent 8-byte loads, 8 per thread
-// per batch, into LDS (swizzled 16-byte granules, row stride p.hstride).
-__device__ __forceinline__ void stage_h(const LayerParams& p, u32x4* hs, const float* src, const Lds& L, int g0,
-                                        int nr, int K) {
+// h rows (tagged pairs written earlier in this launch) of rows [g0, g0+nr),
+// row r taken from src[slot(r)], polled until every pair carries this call's
+// tag, into LDS as fp32 (swizzled 16-byte granules, row stride p.hstride).
+// 8 pairs per thread per batch.
+__device__ __forceinline__ void stage_h(const LayerParams& p, const WgState& st, u32x4* hs, const uint64_t* src,
+                                        const Lds& L, int g0, int nr, int K) {
   __syncthreads();
-  const int per_row = K / 2, total = nr * per_row;
-  uint64_t* h64 = reinterpret_cast<uint64_t*>(hs);
+  const int total = nr * K;
+  float* hf = reinterpret_cast<float*>(hs);
+  bool ok = true;
   for (int base = threadIdx.x; base < total; base += 256 * 8) {
     uint64_t v[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int i = min(base + 256 * t, total - 1);
-      const int r = i / per_row, c = i - r * per_row;
-      v[t] = ld_coh64(src + (size_t)L.slot[g0 + r] * K + 2 * c);
-    }
+    const int n = min(8, (total - base + 255) / 256);
+    ok &= poll_pairs<8>(src, n, [&](int t) {
+      const int i = base + 256 * t;
+      const int r = i / K, e = i - r * K;
+      return (size_t)L.slot[g0 + r] * K + e;
+    }, st.tag, v, SPIN_LIMIT, p.ctrl + CTRL_ERR);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int i = base + 256 * t;
       if (i < total) {
-        const int r = i / per_row, c = i - r * per_row;  // u64 c = granule c/2, half c%2
-        h64[2 * (r * p.hstride + swz(c >> 1)) + (c & 1)] = v[t];
+        const int r = i / K, e = i - r * K;
+        hf[(r * p.hstride + swz(e >> 2)) * 4 + (e & 3)] = pair_f32(v[t]);
       }
     }
   }
+  if (!ok) set_error(p);
   __syncthreads();
 }
 
@@ -274,86 +275,6 @@ __device__ __forceinline__ void stage_h(const LayerParams& p, u32x4* hs, const f
 // or masked (the case at the K3 shapes); otherwise loads are clamped and the
 // overhang masked.
 template <int RG, bool FULL>
-struct Fc1Mx {
-  const uint8_t *codes, *scales;  // this lane's matrix (gate or up), row 0
-  int H, C, nseg, n0;
-  const u32x4* xs;  // LDS x rows (swizzled)
-  int xstride;
-  int nr;
-  float acc[RG];
-  float* out;  // h rows, indexed by slot
-  int out_ld;
-  const int* slot;
-  __device__ void load(MxBuf<CPL1>& b, int p) {
-    const int i = p / nseg, s = p - i * nseg, n = n0 + 4 * i;
-    const int l = threadIdx.x & 31;
-    const int c0 = s * 32 * CPL1 + l;
-    const uint8_t* cr = codes + (size_t)n * (H / 2) + 16 * c0;
-    const uint8_t* sr = scales + (size_t)n * (H / 32) + c0;
-#pragma unroll
-    for (int ci = 0; ci < CPL1; ++ci) {
-      const int dc = FULL ? 32 * ci : min(c0 + 32 * ci, C - 1) - c0;
-      b.q[ci] = ld_weight16(cr + 16 * dc);
-      if (!FULL) b.s[ci] = sr[dc];
-    }
-    if (FULL) {  // this half-wave's 224 scale bytes of the segment: two dwords per lane
-      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(scales + (size_t)n * (H / 32) + s * 32 * CPL1);
-      b.sa = __builtin_nontemporal_load(s32 + l);
-      b.sb = __builtin_nontemporal_load(s32 + 32 + min(l, 8 * CPL1 - 33));
-    }
-  }
-  __device__ void math(const MxBuf<CPL1>& b, int p) {
-    const int i = p / nseg, s = p - i * nseg;
-    const int lane = threadIdx.x & 63, l = lane & 31;
-#pragma unroll
-    for (int ci = 0; ci < CPL1; ++ci) {
-      const int craw = s * 32 * CPL1 + l + 32 * ci;
-      const int c = FULL ? craw : min(craw, C - 1);
-      const uint32_t msk = (FULL || craw < C) ? 0xFFFFFFFFu : 0u;
-      uint32_t sbyte;
-      if (FULL) {  // byte l + 32 ci of the segment = dword l/4 + 8 ci, held by lane (l/4 + 8 ci) mod 32
-        const int q = (l >> 2) + 8 * ci;
-        const uint32_t wv = __shfl(ci < 4 ? b.sa : b.sb, (lane & 32) | (q & 31), WAVE);
-        sbyte = (wv >> (8 * (l & 3))) & 0xFFu;
-      } else {
-        sbyte = b.s[ci];
-      }
-      const float sc = e8m0_scale(sbyte);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        bf16x2 w[4];
-        dq4_bf16(FULL ? b.q[ci][d] : (b.q[ci][d] & msk), sc, w);
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          if (RG == 1 || r < nr) {
-            const u32x4 xv = xs[r * xstride + swz(4 * c + d)];
-            float a = acc[r];
-            a = dot2_bf16(w[0], xv[0], a);
-            a = dot2_bf16(w[1], xv[1], a);
-            a = dot2_bf16(w[2], xv[2], a);
-            a = dot2_bf16(w[3], xv[3], a);
-            acc[r] = a;
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep each chunk's LDS reads and dequant local
-    }
-    if (s == nseg - 1) {
-      const int n = n0 + 4 * i;
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        if (RG == 1 || r < nr) {
-          const float g = sum_lanes<32>(acc[r]);
-          const float u = __shfl(g, 32, WAVE);
-          if (lane == 0) st_coh(out + (size_t)slot[r] * out_ld + n, silu_f(g) * u);
-        }
-        acc[r] = 0.0f;
-      }
-    }
-  }
-};
-
-template <int RG, bool FULL>
 struct Fc1Bf {
   const uint16_t* w;  // this lane's matrix (gate or up), row 0
   int H, C8, nseg, n0;
@@ -361,7 +282,8 @@ struct Fc1Bf {
   int xstride;
   int nr;
   float acc[RG];
-  float* out;  // h_shared rows, indexed by batch row
+  uint64_t* out;  // shared h pairs, indexed by batch row
+  uint32_t tag;
   int out_ld;
   const int* row;
   __device__ void load(BfBuf<CPL1>& b, int p) {
@@ -405,94 +327,7 @@ struct Fc1Bf {
         if (RG == 1 || r < nr) {
           const float g = sum_lanes<32>(acc[r]);
           const float u = __shfl(g, 32, WAVE);
-          if (lane == 0) st_coh(out + (size_t)row[r] * out_ld + n, silu_f(g) * u);
-        }
-        acc[r] = 0.0f;
-      }
-    }
-  }
-};
-
-template <int RG, bool FULL>
-struct Fc2Mx {
-  const uint8_t *codes, *scales;  // down matrix row 0
-  int K, C, nseg, m_begin, m_end;
-  const u32x4* hs;  // LDS h rows (swizzled)
-  int hstride;
-  int nr;
-  float acc[RG];
-  float* out;  // o_routed rows, indexed by slot
-  int out_ld;
-  const int* slot;
-  __device__ int row_of(int grp) const {
-    return m_begin + ((threadIdx.x >> 6) + 4 * grp) * 8 + ((threadIdx.x & 63) >> 3);
-  }
-  __device__ void load(MxBuf<CPL2>& b, int p) {
-    const int grp = p / nseg, s = p - grp * nseg;
-    const int m = FULL ? row_of(grp) : min(row_of(grp), m_end - 1);
-    const int l = threadIdx.x & 7;
-    const int c0 = s * 8 * CPL2 + l;
-    const uint8_t* cr = codes + (size_t)m * (K / 2) + 16 * c0;
-    const uint8_t* sr = scales + (size_t)m * (K / 32) + c0;
-#pragma unroll
-    for (int ci = 0; ci < CPL2; ++ci) {
-      const int dc = FULL ? 8 * ci : min(c0 + 8 * ci, C - 1) - c0;
-      b.q[ci] = ld_weight16(cr + 16 * dc);
-      if (!FULL) b.s[ci] = sr[dc];
-    }
-    if (FULL) {  // this 8-lane group's 48 scale bytes of the segment: two dwords per lane
-      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(scales + (size_t)m * (K / 32) + s * 8 * CPL2);
-      b.sa = __builtin_nontemporal_load(s32 + l);
-      b.sb = __builtin_nontemporal_load(s32 + 8 + min(l, 2 * CPL2 - 9));
-    }
-  }
-  __device__ void math(const MxBuf<CPL2>& b, int p) {
-    const int grp = p / nseg, s = p - grp * nseg, m = row_of(grp);
-    const int lane = threadIdx.x & 63, l = lane & 7;
-#pragma unroll
-    for (int ci = 0; ci < CPL2; ++ci) {
-      const int craw = s * 8 * CPL2 + l + 8 * ci;
-      const int c = FULL ? craw : min(craw, C - 1);
-      const uint32_t msk = (FULL || craw < C) ? 0xFFFFFFFFu : 0u;
-      uint32_t sbyte;
-      if (FULL) {  // byte l + 8 ci = dword l/4 + 2 ci, held by group lane (l/4 + 2 ci) mod 8
-        const int q = (l >> 2) + 2 * ci;
-        const uint32_t wv = __shfl(ci < 4 ? b.sa : b.sb, (lane & ~7) | (q & 7), WAVE);
-        sbyte = (wv >> (8 * (l & 3))) & 0xFFu;
-      } else {
-        sbyte = b.s[ci];
-      }
-      const float sc = e8m0_scale(sbyte);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        f32x2 w[4];
-        dq4_f32(FULL ? b.q[ci][d] : (b.q[ci][d] & msk), sc, w);
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          if (RG == 1 || r < nr) {
-            const f32x4 x0 = __builtin_bit_cast(f32x4, hs[r * hstride + swz(8 * c + 2 * d)]);
-            const f32x4 x1 = __builtin_bit_cast(f32x4, hs[r * hstride + swz(8 * c + 2 * d + 1)]);
-            float a = acc[r];
-            a = fmaf(w[0].x, x0.x, a);
-            a = fmaf(w[0].y, x0.y, a);
-            a = fmaf(w[1].x, x0.z, a);
-            a = fmaf(w[1].y, x0.w, a);
-            a = fmaf(w[2].x, x1.x, a);
-            a = fmaf(w[2].y, x1.y, a);
-            a = fmaf(w[3].x, x1.z, a);
-            a = fmaf(w[3].y, x1.w, a);
-            acc[r] = a;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // one dword of codes at a time
-      }
-    }
-    if (s == nseg - 1) {
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        if (RG == 1 || r < nr) {
-          const float v = sum_lanes<8>(acc[r]);
-          if (l == 0 && (FULL || m < m_end)) st_coh(out + (size_t)slot[r] * out_ld + m, v);
+          if (lane == 0) st_pair_f32(out + (size_t)row[r] * out_ld + n, silu_f(g) * u, tag);
         }
         acc[r] = 0.0f;
       }
@@ -508,7 +343,8 @@ struct Fc2Bf {
   int hstride;
   int nr;
   float acc[RG];
-  float* out;  // o_shared rows, indexed by batch row
+  uint64_t* out;  // shared output pairs, indexed by batch row
+  uint32_t tag;
   int out_ld;
   const int* row;
   __device__ int row_of(int grp) const {
@@ -559,7 +395,7 @@ struct Fc2Bf {
       for (int r = 0; r < RG; ++r) {
         if (RG == 1 || r < nr) {
           const float v = sum_lanes<8>(acc[r]);
-          if (l == 0 && (FULL || m < m_end)) st_coh(out + (size_t)row[r] * out_ld + m, v);
+          if (l == 0 && (FULL || m < m_end)) st_pair_f32(out + (size_t)row[r] * out_ld + m, v, tag);
         }
         acc[r] = 0.0f;
       }
@@ -567,31 +403,246 @@ struct Fc2Bf {
   }
 };
 
-// ---- units --------------------------------------------------------------------
+// ---- packed-tile streams of the routed experts ---------------------------------
+//
+// An expert's MXFP4 matrices are packed (moe_pack_experts) into tiles of 16
+// rows x 16 blocks of 32 elements: codes [SC][16 rows] x 16 B, then scales
+// [16 rows][SC] B.  Lane l = 16 q + r of a wave reads, from 1 KB slab kb of a
+// tile, block 4 kb + q of row r: each load instruction is one contiguous KB.
+// A lane therefore accumulates row r over blocks q, q+4, q+8, ...; the four
+// lanes r, r+16, r+32, r+48 are summed at the end of the row.
 
-__device__ __forceinline__ unsigned* ctrl_at(const LayerParams& p, int line) { return p.ctrl + ctrl_word(line); }
-__device__ __forceinline__ int line_fc1(int a) { return CTRL_FC1 + a; }
-__device__ __forceinline__ int line_tile(const LayerParams& p, int t) { return CTRL_FC1 + p.umax + t; }
-__device__ __forceinline__ int line_rb(const LayerParams& p, int rb) { return CTRL_FC1 + p.umax + p.T2 + rb; }
-__device__ __forceinline__ int line_pub(const LayerParams& p, int j) {
-  return CTRL_FC1 + p.umax + p.T2 + MOE_MAX_BATCH + j;
+__host__ __device__ inline size_t tile_off(int g, int s, int C) {
+  return (size_t)g * 16 * C * 17 + (size_t)s * 16 * 272;
 }
 
-// Expert-gathered schedule from idx[B][k] (LDS counting; 256 threads).
-// LDS: cnt[E], start[E], ids[B*k].
-__device__ void build_schedule(const LayerParams& p, int* cnt, int* wtot /* LDS [8] */) {
+struct TileBuf1 {  // one FC1 segment: gate and up codes (4 slabs each) and scale vectors
+  u32x4 gq[4], uq[4];
+  u32x4 gs, us;
+};
+
+struct TileBuf2 {  // one FC2 segment of two row groups
+  u32x4 q[2][4];
+  u32x4 s[2];
+};
+
+// Scale byte of block 4 kb + q of this lane's row: FULL tiles hold the row's
+// 16 scale bytes as one 16-byte vector; partial tiles gather the 4 bytes the
+// lane needs into the first dword (byte kb).
+template <bool FULL>
+__device__ __forceinline__ uint32_t tile_scale(const u32x4& v, int kb, int q) {
+  return FULL ? (v[kb] >> (8 * q)) & 0xFFu : (v[0] >> (8 * kb)) & 0xFFu;
+}
+
+template <bool FULL>
+__device__ __forceinline__ void load_tile(const uint8_t* t, int SC, u32x4 (&cq)[4], u32x4& sv) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  if (FULL) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) cq[kb] = ld_weight16(t + kb * 1024 + l * 16);
+    sv = ld_weight16(t + 4096 + r * 16);
+  } else {
+    uint32_t b = 0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int c = min(4 * kb + q, SC - 1);
+      cq[kb] = ld_weight16(t + c * 256 + r * 16);
+      b |= (uint32_t)t[SC * 256 + r * SC + c] << (8 * kb);
+    }
+    sv = u32x4{b, 0u, 0u, 0u};
+  }
+}
+
+// The LDS reads of a pass's activations are software-pipelined one step
+// ahead of the math, and each read's address is tied (through an empty asm)
+// to the accumulator of the step before, so the compiler cannot hoist every
+// read of the pass to its top: that would hold 16-32 granules (64-128
+// VGPRs) live and push the kernel into spilling.
+__device__ __forceinline__ int after(int idx, float dep) {
+  asm volatile("" : "+v"(idx) : "v"(dep));
+  return idx;
+}
+
+// FC1 + SwiGLU of one 16-row group g of an expert against RG rows of x (LDS).
+// Wave w takes segments w, w+4, ...; partial sums meet in LDS afterwards.
+template <int RG, bool FULL>
+struct Fc1Tile {
+  const uint8_t* blob;
+  int C1, g, w;
+  const u32x4* xs;
+  int xstride;
+  int nr;
+  float ag[RG], au[RG];
+  __device__ int seg(int p) const { return w + 4 * p; }
+  __device__ void load(TileBuf1& b, int p) {
+    const int s = seg(p);
+    const int SC = FULL ? 16 : min(16, C1 - 16 * s);
+    // issued only after the math of the pass before (its accumulator), so the
+    // compiler cannot start this pass's loads early and hold a third buffer
+    const uint8_t* gt = blob + 2 * tile_off(g, s, C1) + after(after(0, ag[0]), au[0]);
+    load_tile<FULL>(gt, SC, b.gq, b.gs);
+    load_tile<FULL>(gt + SC * 272, SC, b.uq, b.us);
+  }
+  // x granule of step i = 4 kb + d (block 4 kb + q of the segment)
+  __device__ int xg(int s, int SC, int i) const {
+    const int q = (threadIdx.x & 63) >> 4, c = 4 * (i >> 2) + q;
+    return swz((16 * s + (FULL ? c : min(c, SC - 1))) * 4 + (i & 3));
+  }
+  __device__ void math(const TileBuf1& b, int p) {
+    const int s = seg(p);
+    const int q = (threadIdx.x & 63) >> 4;
+    const int SC = FULL ? 16 : min(16, C1 - 16 * s);
+    u32x4 xv[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) xv[r] = (RG == 1 || r < nr) ? xs[r * xstride + xg(s, SC, 0)] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kb = i >> 2, d = i & 3;
+      u32x4 xn[RG];
+      if (i < 15) {
+        const int gi = after(after(xg(s, SC, i + 1), ag[0]), au[0]);
+#pragma unroll
+        for (int r = 0; r < RG; ++r) xn[r] = (RG == 1 || r < nr) ? xs[r * xstride + gi] : u32x4{0u, 0u, 0u, 0u};
+      }
+      const int c = 4 * kb + q;
+      const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
+      const float sg = e8m0_scale(tile_scale<FULL>(b.gs, kb, q));
+      const float su = e8m0_scale(tile_scale<FULL>(b.us, kb, q));
+      bf16x2 wg[4], wu[4];
+      dq4_bf16(b.gq[kb][d] & msk, sg, wg);
+      dq4_bf16(b.uq[kb][d] & msk, su, wu);
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        if (RG == 1 || r < nr) {
+          float a0 = ag[r], a1 = au[r];
+          a0 = dot2_bf16(wg[0], xv[r][0], a0);
+          a1 = dot2_bf16(wu[0], xv[r][0], a1);
+          a0 = dot2_bf16(wg[1], xv[r][1], a0);
+          a1 = dot2_bf16(wu[1], xv[r][1], a1);
+          a0 = dot2_bf16(wg[2], xv[r][2], a0);
+          a1 = dot2_bf16(wu[2], xv[r][2], a1);
+          a0 = dot2_bf16(wg[3], xv[r][3], a0);
+          a1 = dot2_bf16(wu[3], xv[r][3], a1);
+          ag[r] = a0;
+          au[r] = a1;
+        }
+      }
+      if (i < 15) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) xv[r] = xn[r];
+      }
+    }
+  }
+};
+
+// FC2 of up to two 16-row groups (g0 and g0 + 4) of the down matrix against
+// RG rows of h (fp32, LDS); one pass per segment along I.
+template <int RG, bool FULL>
+struct Fc2Tile {
+  const uint8_t* down;  // packed down region of the blob
+  int C2, g0, ng;
+  const u32x4* hs;
+  int hstride;
+  int nr;
+  float acc[2][RG];
+  __device__ void load(TileBuf2& b, int s) {
+    const int SC = FULL ? 16 : min(16, C2 - 16 * s);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      load_tile<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s, C2) + after(after(0, acc[0][0]), acc[1][0]), SC, b.q[t], b.s[t]);
+  }
+  // first h granule (4 floats) of step i = 4 kb + d: elements 8 d .. 8 d + 7 of block 4 kb + q
+  __device__ int hg(int s, int SC, int i) const {
+    const int q = (threadIdx.x & 63) >> 4, c = 4 * (i >> 2) + q;
+    return (16 * s + (FULL ? c : min(c, SC - 1))) * 8 + 2 * (i & 3);
+  }
+  __device__ void math(const TileBuf2& b, int s) {
+    const int q = (threadIdx.x & 63) >> 4;
+    const int SC = FULL ? 16 : min(16, C2 - 16 * s);
+    f32x4 x0[RG], x1[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int g = hg(s, SC, 0);
+      x0[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g)]) : f32x4{0, 0, 0, 0};
+      x1[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g + 1)]) : f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kb = i >> 2, d = i & 3;
+      f32x4 n0[RG], n1[RG];
+      if (i < 15) {
+        const int g = after(after(hg(s, SC, i + 1), acc[0][0]), acc[1][0]);
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          n0[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g)]) : f32x4{0, 0, 0, 0};
+          n1[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g + 1)]) : f32x4{0, 0, 0, 0};
+        }
+      }
+      const int c = 4 * kb + q;
+      const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
+      f32x2 w0[4], w1[4];
+      dq4_f32(b.q[0][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[0], kb, q)), w0);
+      dq4_f32(b.q[1][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[1], kb, q)), w1);
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        if (RG == 1 || r < nr) {
+          float a = acc[0][r], e = acc[1][r];
+          a = fmaf(w0[0].x, x0[r].x, a);
+          e = fmaf(w1[0].x, x0[r].x, e);
+          a = fmaf(w0[0].y, x0[r].y, a);
+          e = fmaf(w1[0].y, x0[r].y, e);
+          a = fmaf(w0[1].x, x0[r].z, a);
+          e = fmaf(w1[1].x, x0[r].z, e);
+          a = fmaf(w0[1].y, x0[r].w, a);
+          e = fmaf(w1[1].y, x0[r].w, e);
+          a = fmaf(w0[2].x, x1[r].x, a);
+          e = fmaf(w1[2].x, x1[r].x, e);
+          a = fmaf(w0[2].y, x1[r].y, a);
+          e = fmaf(w1[2].y, x1[r].y, e);
+          a = fmaf(w0[3].x, x1[r].z, a);
+          e = fmaf(w1[3].x, x1[r].z, e);
+          a = fmaf(w0[3].y, x1[r].w, a);
+          e = fmaf(w1[3].y, x1[r].w, e);
+          acc[0][r] = a;
+          acc[1][r] = e;
+        }
+      }
+      if (i < 15) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          x0[r] = n0[r];
+          x1[r] = n1[r];
+        }
+      }
+    }
+  }
+};
+
+// Sum over the four lanes r, r+16, r+32, r+48 that share a tile row.
+__device__ __forceinline__ float sum_q(float v) {
+  v += __shfl_xor(v, 16, WAVE);
+  v += __shfl_xor(v, 32, WAVE);
+  return v;
+}
+
+// ---- units --------------------------------------------------------------------
+
+// Expert-gathered schedule from the routing pairs of all B*k slots (LDS
+// counting; 256 threads).  LDS: cnt[E], start[E], ids[B*k].
+__device__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt, int* wtot /* LDS [8] */) {
   int* start = cnt + p.E;
   int* ids = start + p.E;
   const int t = threadIdx.x, nslots = p.B * p.k;
-  // every slot's expert id, coherent loads in batches of 4 per thread
-  for (int base = t; base < nslots; base += 256 * 4) {
-    int v[4];
+  bool ok = true;
+  for (int base = t; base < nslots; base += 256 * 8) {
+    uint64_t v[8];
+    const int n = min(8, (nslots - base + 255) / 256);
+    ok &= poll_pairs<8>(p.idx_p, n, [&](int i) { return base + 256 * i; }, st.tag, v, SPIN_LIMIT, p.ctrl + CTRL_ERR);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ld_coh(p.idx + min(base + 256 * i, nslots - 1));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (base + 256 * i < nslots) ids[base + 256 * i] = v[i];
+    for (int i = 0; i < 8; ++i)
+      if (base + 256 * i < nslots) ids[base + 256 * i] = (int)min((uint32_t)v[i], (uint32_t)p.E - 1u);
   }
+  if (!ok) set_error(p);
   for (int e = t; e < p.E; e += 256) cnt[e] = 0;
   __syncthreads();
   for (int s = t; s < nslots; s += 256) atomicAdd(&cnt[ids[s]], 1);
@@ -638,56 +689,23 @@ __device__ void build_schedule(const LayerParams& p, int* cnt, int* wtot /* LDS 
       pr += cnt[e];
     }
   }
-  if (t == 255) {
-    st_coh(p.row_off + base_a + ia, base_r + ir);
-    st_coh(ctrl_at(p, CTRL_U), (unsigned)(base_a + ia));
-  }
+  if (t == 255) st_coh(p.row_off + base_a + ia, base_r + ir);
   __syncthreads();
   for (int s = t; s < nslots; s += 256) {
     const int pos = atomicAdd(&start[ids[s]], 1);
     st_coh(p.rows + pos, s);
   }
-}
-
-// Routing of rows [b0, b0+nr), run by the workgroup that completed their
-// logits.  Top-k keys and candidates live in LDS (the x region): routing runs
-// a handful of times per call, and holding its state in registers would set
-// the register budget -- and so the occupancy -- of the whole kernel.
-//   batch 1: each selected expert is published at once in its slot's counter
-//            line (expert + 1), which is all a routed unit needs;
-//   batch > 1: the workgroup that routes the last rows inverts the routing
-//            into the expert-gathered schedule and publishes READY.
-template <int TPL>
-__device__ void route_rows(const LayerParams& p, WgState& st, Lds& L, int* lds_ints, int b0, int nr) {
-  __builtin_amdgcn_s_setprio(3);  // on the critical path: issue ahead of streaming waves
-  for (int r = 0; r < nr; ++r) {
-    __syncthreads();  // the LDS region is reused
-    const int b = b0 + r;
-    const int myx = topk_row_wg<TPL>(p.logits + (size_t)b * p.E, p.E, p.k, reinterpret_cast<uint32_t*>(lds_ints),
-                                     p.idx + (size_t)b * p.k, p.gate + (size_t)b * p.k);
-    if (p.B == 1 && threadIdx.x < p.k) {
-      __builtin_amdgcn_s_waitcnt(0);  // this lane's idx and gate stores are complete
-      st_coh(ctrl_at(p, line_pub(p, threadIdx.x)), (unsigned)myx + 1u);
-    }
-  }
-  st.x_cached = false;
-  if (p.B > 1) {
-    const unsigned old = wg_signal_add(ctrl_at(p, CTRL_ROUTING));
-    if (threadIdx.x == 0) L.flag = (old == (unsigned)p.n_rb - 1);
-    __syncthreads();
-    if (L.flag) {
-      build_schedule(p, lds_ints, L.wtot);
-      wg_signal_add(ctrl_at(p, CTRL_READY));
-    }
-  }
-  __builtin_amdgcn_s_setprio(0);
+  // publish: every thread's schedule stores complete, then the ready word
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t == 0)
+    st_coh(reinterpret_cast<uint64_t*>(p.ctrl + CTRL_READY), make_pair((uint32_t)(wtot[4] + wtot[5] + wtot[6] + wtot[7]), st.tag));
 }
 
 // Router unit: experts 2u and 2u+1 for a block of rows.  Waves 0-1 take the
 // two halves of expert 2u's row, waves 2-3 those of expert 2u+1, so every wave
-// streams 7 KB at H 7168 in one pass of loads; the halves meet in LDS.  The
-// last unit of a row block to finish routes its rows.
-template <int RG, int TPL>
+// streams 7 KB at H 7168 in one pass of loads; the halves meet in LDS.
+template <int RG>
 __device__ void router_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int u) {
   const int pe = u % p.n_rt_e, rb = u / p.n_rt_e;
   const int b0 = rb * RG, nr = min(RG, p.B - b0);
@@ -707,43 +725,28 @@ __device__ void router_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs
     const double bb = p.bias ? (double)p.bias[e] : 0.0;
 #pragma unroll
     for (int r = 0; r < RG; ++r)
-      if (r < nr) st_coh(p.logits + (size_t)(b0 + r) * p.E + e, (float)(acc[r] + L.part[w + 1][r] + bb));
+      if (r < nr) st_pair_f32(p.logits_p + (size_t)(b0 + r) * p.E + e, (float)(acc[r] + L.part[w + 1][r] + bb), st.tag);
   }
-  const unsigned old = wg_signal_add(ctrl_at(p, line_rb(p, rb)));
-  if (threadIdx.x == 0) L.flag = (old == (unsigned)p.n_rt_e - 1);
-  __syncthreads();
-  if (L.flag) route_rows<TPL>(p, st, L, reinterpret_cast<int*>(xs), b0, nr);
 }
 
-// Batch 1: wait until slot a's expert is published (and, if fc1_target > 0,
-// until that many FC1 units of the slot are done); both counters are read in
-// one round trip per poll.  Sets the unit's row list to the slot itself.
-__device__ __forceinline__ int wait_slot(const LayerParams& p, Lds& L, int a, unsigned fc1_target) {
-  if (threadIdx.x == 0) {
-    const unsigned* pub = ctrl_at(p, line_pub(p, a));
-    const unsigned* done = ctrl_at(p, line_fc1(a));
-    unsigned it = 0, nap = 1, v;
-    for (;;) {
-      v = ld_ctrl(pub);
-      const unsigned c = fc1_target ? ld_ctrl(done) : 0u;
-      if (v != 0u && c >= fc1_target) break;
-      if (nap <= 1) __builtin_amdgcn_s_sleep(1);
-      else if (nap <= 4) __builtin_amdgcn_s_sleep(4);
-      else __builtin_amdgcn_s_sleep(16);
-      nap = nap < 32 ? 2 * nap : 32;
-      if (++it >= SPIN_LIMIT) {
-        __hip_atomic_fetch_or(ctrl_at(p, CTRL_ERR), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v = 1u;
-        break;
-      }
-    }
-    L.expert = (int)min(v - 1u, (unsigned)p.E - 1u);
-    L.slot[0] = a;
-    L.nrows = 1;
-  }
+// Routing unit of row b: top-k over the row's logits (polled until the router
+// has written them all) and the gates.  Top-k state lives in LDS (the x
+// region): holding it in registers would set the register budget -- and so
+// the occupancy -- of the whole kernel.
+template <int TPL>
+__device__ void routing_unit(const LayerParams& p, WgState& st, Lds& L, int* lds_ints, int b) {
+  __builtin_amdgcn_s_setprio(3);  // on the critical path: issue ahead of streaming waves
+  __syncthreads();                // the LDS region is reused
+  const size_t s0 = (size_t)b * p.k;
+  uint32_t* cand = reinterpret_cast<uint32_t*>(lds_ints);
+  topk_row_wg<TPL>(p.logits_p + (size_t)b * p.E, p.E, p.k, st.tag, SPIN_LIMIT, p.ctrl + CTRL_ERR, cand, p.idx + s0,
+                   p.gate + s0, p.idx_p + s0, p.gate_p + s0, true);
   __syncthreads();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return L.expert;
+  if (!topk_row_wg<TPL>(p.logits_p + (size_t)b * p.E, p.E, p.k, st.tag, SPIN_LIMIT, p.ctrl + CTRL_ERR, cand,
+                        p.idx + s0, p.gate + s0, p.idx_p + s0, p.gate_p + s0, false))
+    set_error(p);
+  st.x_cached = false;
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int RG, bool FULL>
@@ -763,7 +766,8 @@ __device__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.xstride = p.xstride;
     f.nr = nr;
     for (int r = 0; r < RG; ++r) f.acc[r] = 0.0f;
-    f.out = p.h_shared;
+    f.out = p.hs_p;
+    f.tag = st.tag;
     f.out_ld = p.Is;
     f.row = L.slot + g0;
     const int nrows = f.n0 < n_end ? (n_end - f.n0 + 3) / 4 : 0;
@@ -773,81 +777,60 @@ __device__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     stage_x(p, st, L, xs, false, g0, nr);
     drive_passes(f, P, ba, bb);
   }
-  wg_signal_add(ctrl_at(p, CTRL_SH1));
 }
 
+// Routed FC1 + SwiGLU of row group g (16 rows of I) of active expert a, for
+// all of the expert's rows (RG at a time).
 template <int RG, bool FULL>
-__device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int t) {
-  int expert;
-  if (p.B == 1) {
-    expert = wait_slot(p, L, a, 0u);
-  } else {
-    load_rows(p, st, L, a);
-    expert = st.s_active[a];
-  }
+__device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g) {
+  load_rows(p, st, L, a);
   const int nrows_unit = L.nrows;
-  const uint8_t* blob = p.experts + (size_t)expert * p.blob_bytes;
-  const int half = (threadIdx.x & 63) >> 5;
-  const int n_begin = t * NT1, n_end = min(p.I, n_begin + NT1);
+  const uint8_t* blob = p.experts + (size_t)st.s_active[a] * p.blob_bytes;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C1 = p.H / 32, S1 = (C1 + 15) / 16;
+  const int P = w < S1 ? (S1 - w + 3) / 4 : 0;
   for (int g0 = 0; g0 < nrows_unit; g0 += RG) {
     const int nr = min(RG, nrows_unit - g0);
-    Fc1Mx<RG, FULL> f;
-    f.codes = blob + p.off[half];
-    f.scales = blob + p.off[3 + half];
-    f.H = p.H;
-    f.C = p.H / 32;
-    f.nseg = (f.C + 32 * CPL1 - 1) / (32 * CPL1);
-    f.n0 = n_begin + (threadIdx.x >> 6);
+    Fc1Tile<RG, FULL> f;
+    f.blob = blob;
+    f.C1 = C1;
+    f.g = g;
+    f.w = w;
     f.xs = xs;
     f.xstride = p.xstride;
     f.nr = nr;
-    for (int r = 0; r < RG; ++r) f.acc[r] = 0.0f;
-    f.out = p.h_routed;
-    f.out_ld = p.I;
-    f.slot = L.slot + g0;
-    const int nrows = f.n0 < n_end ? (n_end - f.n0 + 3) / 4 : 0;
-    const int P = nrows * f.nseg;
-    MxBuf<CPL1> ba, bb;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) f.ag[r] = f.au[r] = 0.0f;
+    TileBuf1 ba, bb;
     prime_passes(f, P, ba, bb);
     stage_x(p, st, L, xs, true, g0, nr);
     drive_passes(f, P, ba, bb);
-  }
-  wg_signal_add(ctrl_at(p, line_fc1(a)));
-}
-
-// After a FC2 unit of tile t: count it; the last contribution folds the tile
-// into the residual (fixed order: shared, then j = 0..k-1).
-__device__ void fc2_ticket(const LayerParams& p, int U, Lds& L, int t) {
-  const unsigned expected = (unsigned)((p.Is > 0 ? SUB2 : 0) + SUBR * U);
-  const unsigned old = wg_signal_add(ctrl_at(p, line_tile(p, t)));
-  if (threadIdx.x == 0) L.flag = (old == expected - 1);
-  __syncthreads();
-  if (!L.flag) return;
-  const int m_begin = t * NT2, m_end = min(p.H, m_begin + NT2), w = m_end - m_begin;
-  for (int i = threadIdx.x; i < p.B * w; i += 256) {
-    const int b = i / w, m = m_begin + (i - b * w);
-    float acc = p.residual[(size_t)b * p.H + m];
-    if (p.Is > 0) acc += ld_coh(p.o_shared + (size_t)b * p.H + m);
-    for (int j0 = 0; j0 < p.k; j0 += 8) {  // 16 coherent loads per batch
-      float gv[8], ov[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = min(j0 + q, p.k - 1);
-        gv[q] = ld_coh(p.gate + b * p.k + j);
-        ov[q] = ld_coh(p.o_routed + ((size_t)b * p.k + j) * p.H + m);
+    for (int r = 0; r < RG; ++r) {
+      const float vg = sum_q(f.ag[r]), vu = sum_q(f.au[r]);
+      if (lane < 16) {
+        L.red[w][r][lane][0] = vg;
+        L.red[w][r][lane][1] = vu;
       }
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (j0 + q < p.k) acc = fmaf(gv[q], ov[q], acc);
     }
-    p.residual[(size_t)b * p.H + m] = acc;
+    __syncthreads();
+    if ((int)threadIdx.x < nr * 16) {
+      const int r = threadIdx.x >> 4, row = threadIdx.x & 15;
+      float vg = 0.0f, vu = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        vg += L.red[ww][r][row][0];
+        vu += L.red[ww][r][row][1];
+      }
+      st_pair_f32(p.hr_p + (size_t)L.slot[g0 + r] * p.I + 16 * g + row, silu_f(vg) * vu, st.tag);
+    }
+    __syncthreads();
   }
 }
 
 template <int RG, bool FULL>
 __device__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int v) {
-  const int t = v / SUB2, sub = v - t * SUB2;
-  const int m_begin = t * NT2 + sub * NTS2, m_end = min(p.H, m_begin + NTS2);
+  const int m_begin = v * NTS2, m_end = min(p.H, m_begin + NTS2);
   load_rows(p, st, L, -1);
   for (int g0 = 0; g0 < p.B; g0 += RG) {
     const int nr = min(RG, p.B - g0);
@@ -862,70 +845,92 @@ __device__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.hstride = p.hstride;
     f.nr = nr;
     for (int r = 0; r < RG; ++r) f.acc[r] = 0.0f;
-    f.out = p.o_shared;
+    f.out = p.os_p;
+    f.tag = st.tag;
     f.out_ld = p.H;
     f.row = L.slot + g0;
     const int groups = (m_end - m_begin + 31) / 32;  // 32 rows per block pass (4 waves x 8)
     const int P = m_begin < m_end ? groups * f.nseg : 0;
     BfBuf<CPL2> ba, bb;
     prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
-    if (g0 == 0) wg_wait_geq(p, ctrl_at(p, CTRL_SH1), (unsigned)p.n_s1);
-    stage_h(p, hs, p.h_shared, L, g0, nr, p.Is);
+    stage_h(p, st, hs, p.hs_p, L, g0, nr, p.Is);
     drive_passes(f, P, ba, bb);
   }
-  fc2_ticket(p, st.U, L, t);
 }
 
+// Routed FC2 of 8 row groups (128 rows of H) of active expert a: wave w
+// takes groups 8v + w and 8v + w + 4 and runs one pass per segment along I.
 template <int RG, bool FULL>
 __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v) {
-  const int t = v / SUBR, sub = v - t * SUBR;
-  const int m_begin = t * NT2 + sub * NTR2, m_end = min(p.H, m_begin + NTR2);
-  int expert;
-  if (p.B == 1) {
-    expert = wait_slot(p, L, a, (unsigned)p.T1);
-  } else {
-    load_rows(p, st, L, a);
-    expert = st.s_active[a];
-  }
+  load_rows(p, st, L, a);
   const int nrows_unit = L.nrows;
-  const uint8_t* blob = p.experts + (size_t)expert * p.blob_bytes;
-  for (int g0 = 0; g0 < nrows_unit; g0 += RG) {
-    const int nr = min(RG, nrows_unit - g0);
-    Fc2Mx<RG, FULL> f;
-    f.codes = blob + p.off[2];
-    f.scales = blob + p.off[5];
-    f.K = p.I;
-    f.C = p.I / 32;
-    f.nseg = (f.C + 8 * CPL2 - 1) / (8 * CPL2);
-    f.m_begin = m_begin;
-    f.m_end = m_end;
+  const int C1 = p.H / 32, C2 = p.I / 32, S2 = (C2 + 15) / 16;
+  const uint8_t* down = p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * C1 * 17;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = p.H / 16, g0 = 8 * v + w;
+  const int ng = g0 < G ? (g0 + 4 < G ? 2 : 1) : 0;
+  const int P = ng > 0 ? S2 : 0;
+  for (int r0 = 0; r0 < nrows_unit; r0 += RG) {
+    const int nr = min(RG, nrows_unit - r0);
+    Fc2Tile<RG, FULL> f;
+    f.down = down;
+    f.C2 = C2;
+    f.g0 = min(g0, G - 1);
+    f.ng = ng;
     f.hs = hs;
     f.hstride = p.hstride;
     f.nr = nr;
-    for (int r = 0; r < RG; ++r) f.acc[r] = 0.0f;
-    f.out = p.o_routed;
-    f.out_ld = p.H;
-    f.slot = L.slot + g0;
-    const int groups = (m_end - m_begin + 31) / 32;
-    const int P = m_begin < m_end ? groups * f.nseg : 0;
-    MxBuf<CPL2> ba, bb;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) f.acc[0][r] = f.acc[1][r] = 0.0f;
+    TileBuf2 ba, bb;
     prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
-    if (g0 == 0 && p.B > 1) wg_wait_geq(p, ctrl_at(p, line_fc1(a)), (unsigned)p.T1);
-    stage_h(p, hs, p.h_routed, L, g0, nr, p.I);
+    stage_h(p, st, hs, p.hr_p, L, r0, nr, p.I);
     drive_passes(f, P, ba, bb);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const float val = sum_q(f.acc[t][r]);
+        if ((RG == 1 || r < nr) && lane < 16 && t < ng)
+          st_pair_f32(p.or_p + (size_t)L.slot[r0 + r] * p.H + 16 * (g0 + 4 * t) + lane, val, st.tag);
+      }
+    }
   }
-  fc2_ticket(p, st.U, L, t);
 }
 
-// Next unit of the in-order queue (the first p.n_static units are handed out
-// by workgroup index; they never wait).
-__device__ __forceinline__ int pop_unit(const LayerParams& p, Lds& L) {
+// Combine unit (row b, tile t of NT2 rows of H): residual += shared output +
+// sum_j gate_j * o_j in fixed j order, polling the outputs until they are
+// this call's.  Thread i owns row m = t*NT2 + i.
+__device__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, int t) {
   __syncthreads();
-  if (threadIdx.x == 0)
-    L.next = p.n_static +
-             (int)__hip_atomic_fetch_add(ctrl_at(p, CTRL_HEAD), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const size_t s0 = (size_t)b * p.k;
+  if (threadIdx.x < p.k) {
+    uint64_t g[1];
+    if (!poll_pairs<1>(p.gate_p + s0, 1, [&](int) { return (int)threadIdx.x; }, st.tag, g, SPIN_LIMIT, p.ctrl + CTRL_ERR))
+      set_error(p);
+    L.gates[threadIdx.x] = pair_f32(g[0]);
+  }
   __syncthreads();
-  return L.next;
+  const int m = t * NT2 + threadIdx.x;
+  if (m >= p.H) return;
+  float acc = p.residual[(size_t)b * p.H + m];
+  bool ok = true;
+  if (p.Is > 0) {
+    uint64_t v[1];
+    ok &= poll_pairs<1>(p.os_p + (size_t)b * p.H + m, 1, [](int) { return 0; }, st.tag, v, SPIN_LIMIT, p.ctrl + CTRL_ERR);
+    acc += pair_f32(v[0]);
+  }
+  for (int j0 = 0; j0 < p.k; j0 += 8) {
+    uint64_t v[8];
+    const int n = min(8, p.k - j0);
+    ok &= poll_pairs<8>(p.or_p + (s0 + j0) * p.H + m, n, [&](int q) { return (size_t)q * p.H; }, st.tag, v,
+                        SPIN_LIMIT, p.ctrl + CTRL_ERR);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < n) acc = fmaf(L.gates[j0 + q], pair_f32(v[q]), acc);
+  }
+  if (!ok) set_error(p);
+  p.residual[(size_t)b * p.H + m] = acc;
 }
 
 // ---- the kernel ------------------------------------------------------------------
@@ -934,57 +939,75 @@ __device__ __forceinline__ int pop_unit(const LayerParams& p, Lds& L) {
 // complete (H % 7168 == 0, I % 1536 == 0, Is % 384 == 0), so the streams need
 // no clamping or masking.
 template <int RG, bool FULL, int TPL>
-__global__ __launch_bounds__(256, RG == 1 ? 3 : 2) void k_moe_layer(LayerParams p) {
+__global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   extern __shared__ u32x4 lds_raw[];
   u32x4* xs = lds_raw;
   u32x4* hs = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(lds_raw) + p.lds_h_off);
+  int* sched_lds = reinterpret_cast<int*>(reinterpret_cast<char*>(lds_raw) + p.lds_sched_off);
   __shared__ Lds L;
-  WgState st{false, false, 0, nullptr, nullptr, nullptr};
-  // First units (router and shared FC1 -- they wait on nothing) by workgroup
-  // index, so the launch ramp does not queue on the head counter.
-  int u = (int)blockIdx.x < p.n_static ? (int)blockIdx.x : pop_unit(p, L);
+  if (threadIdx.x == 0) {
+    const uint32_t epoch = ld_coh(p.ctrl + CTRL_EPOCH);
+    L.tag = (epoch == 0xFFFFFFFFu) ? 1u : epoch + 1u;  // never 0: a cleared workspace holds no valid pair
+  }
+  __syncthreads();
+  WgState st{false, false, 0, L.tag, nullptr, nullptr, nullptr};
+  // The first units (router, routing, shared FC1) go by workgroup index, so
+  // the launch ramp does not queue on the head counter.
+  int u = (int)blockIdx.x < p.n_static ? (int)blockIdx.x : -1;
+  unsigned nxt = 0;
+  if (u < 0) {
+    if (threadIdx.x == 0) L.next = p.n_static + (int)__hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    u = L.next;
+  }
   for (;;) {
+    // the next unit is claimed now; its index is only needed after this one
+    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int rel = u;
     if (rel < p.n_rt) {
-      router_unit<RG, TPL>(p, st, L, xs, rel);
-    } else if ((rel -= p.n_rt) < p.n_s1) {
+      router_unit<RG>(p, st, L, xs, rel);
+    } else if ((rel -= p.n_rt) < p.n_ro) {
+      routing_unit<TPL>(p, st, L, reinterpret_cast<int*>(xs), rel);
+    } else if ((rel -= p.n_ro) < p.n_sch) {
+      __syncthreads();
+      build_schedule(p, st, reinterpret_cast<int*>(xs), L.wtot);
+      st.x_cached = false;
+    } else if ((rel -= p.n_sch) < p.n_s1) {
       shared_fc1_unit<RG, FULL>(p, st, L, xs, rel);
     } else {
       rel -= p.n_s1;
       if (!st.route_seen) {
-        if (p.B == 1) {
-          st.U = p.k;  // one row: k distinct experts, one per slot
-        } else {
-          wg_wait_geq(p, ctrl_at(p, CTRL_READY), 1u);
-          st.U = (int)ld_ctrl(ctrl_at(p, CTRL_U));
-          cache_schedule(p, st, reinterpret_cast<int*>(reinterpret_cast<char*>(lds_raw) + p.lds_sched_off));
-        }
-        st.route_seen = true;
+        __syncthreads();
+        cache_schedule(p, st, L, sched_lds);
       }
       const int U = st.U;
       if (rel < U * p.T1) {
         routed_fc1_unit<RG, FULL>(p, st, L, xs, rel / p.T1, rel % p.T1);
       } else if ((rel -= U * p.T1) < p.n_s2) {
         shared_fc2_unit<RG, FULL>(p, st, L, hs, rel);
-      } else if ((rel -= p.n_s2) < U * p.T2 * SUBR) {
-        routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / (p.T2 * SUBR), rel % (p.T2 * SUBR));
+      } else if ((rel -= p.n_s2) < U * p.n_r2) {
+        routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / p.n_r2, rel % p.n_r2);
+      } else if ((rel -= U * p.n_r2) < p.B * p.n_tile) {
+        combine_unit(p, st, L, rel / p.n_tile, rel % p.n_tile);
       } else {
         break;
       }
     }
-    u = pop_unit(p, L);
+    __syncthreads();
+    if (threadIdx.x == 0) L.next = p.n_static + (int)nxt;
+    __syncthreads();
+    u = L.next;
   }
-  // Exit: the last workgroup out clears the control block for the next call
-  // (all other workgroups have made their final control-block access).
+  // Exit: the last workgroup out resets the queue and advances the epoch (all
+  // other workgroups have made their final control-block access).
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(ctrl_at(p, CTRL_EXIT), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    L.flag = (old == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (L.flag) {
-    for (int i = threadIdx.x; i < p.ctrl_words / CTRL_STRIDE; i += 256)
-      if (i != CTRL_ERR) st_coh(ctrl_at(p, i), 0u);
+    const unsigned old = __hip_atomic_fetch_add(p.ctrl + CTRL_EXIT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gridDim.x - 1) {
+      st_coh(p.ctrl + CTRL_HEAD, 0u);
+      st_coh(p.ctrl + CTRL_EXIT, 0u);
+      st_coh(p.ctrl + CTRL_EPOCH, L.tag);  // the next call's tag is L.tag + 1
+    }
   }
 }
 
@@ -1001,15 +1024,17 @@ struct LaunchShape {
 static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   LaunchShape s;
   s.rg = (B == 1) ? 1 : 4;
-  s.full = (H % (32 * 32 * CPL1) == 0) && (H % (8 * 32 * CPL1) == 0) && (I % (32 * 8 * CPL2) == 0) &&
-           (Is % (8 * 8 * CPL2) == 0) && (H % NT2 == 0);
+  // FULL: every packed tile holds 16 blocks (H, I multiples of 512), every
+  // bf16 shared-expert stream segment is complete, and every unit's rows exist
+  s.full = (H % 512 == 0) && (I % 512 == 0) && (H % (32 * 8 * CPL1) == 0) && (Is % (8 * 8 * CPL2) == 0) &&
+           (Is % NTS1 == 0) && (H % NTR2 == 0) && (H % NTS2 == 0);
   s.xstride = ((H / 8 + 7) / 8) * 8;
   int K2 = I > Is ? I : Is;
   s.hstride = ((K2 / 4 + 7) / 8) * 8;
   size_t x_bytes = (size_t)s.rg * s.xstride * 16;
-  // routing reuses this region: top-k candidates (640 words), then the
+  // routing reuses this region: top-k survivors and slots, then the
   // schedule's counts (2E) and slot ids (B*k)
-  size_t keys_bytes = 640 * 4, cnt_bytes = (size_t)(2 * E + B * k) * 4;
+  size_t keys_bytes = (size_t)topk_lds_words(E <= 1024 ? 4 : 16) * 4, cnt_bytes = (size_t)(2 * E + B * k) * 4;
   size_t sched_bytes = keys_bytes > cnt_bytes ? keys_bytes : cnt_bytes;
   size_t xr = align256(x_bytes > sched_bytes ? x_bytes : sched_bytes);
   s.lds_h_off = (int)xr;
@@ -1033,7 +1058,7 @@ static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
     cached[1] = per_cu;
   }
   const int grid = num_cus() * per_cu;
-  p.n_static = std::min(grid, p.n_rt + p.n_s1);
+  p.n_static = std::min(grid, p.n_front);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
@@ -1058,30 +1083,35 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.residual = a.residual;
   p.idx = idx;
   p.gate = const_cast<float*>(a.gate);
-  p.logits = a.ws.logits;
+  p.logits_p = a.ws.logits_p;
+  p.idx_p = a.ws.idx_p;
+  p.gate_p = a.ws.gate_p;
   p.active = a.ws.sched.active;
   p.row_off = a.ws.sched.row_off;
   p.rows = a.ws.sched.rows;
-  p.h_shared = a.ws.h_shared;
-  p.h_routed = a.ws.h_routed;
-  p.o_shared = a.ws.o_shared;
-  p.o_routed = a.ws.o_routed;
+  p.hs_p = a.ws.hs_p;
+  p.hr_p = a.ws.hr_p;
+  p.os_p = a.ws.os_p;
+  p.or_p = a.ws.or_p;
   p.ctrl = a.ws.ctrl;
   p.umax = a.ws.umax;
-  p.ctrl_words = a.ws.ctrl_words;
   const LaunchShape sh = launch_shape(a.H, a.I, a.E, a.k, a.Is, a.B);
   p.n_rt_e = (a.E + 1) / 2;
   p.xstride = sh.xstride;
   p.hstride = sh.hstride;
-  p.n_rt = p.n_rt_e * ((a.B + sh.rg - 1) / sh.rg);
   p.n_rb = (a.B + sh.rg - 1) / sh.rg;
+  p.n_rt = p.n_rt_e * p.n_rb;
+  p.n_ro = a.B;
+  p.n_sch = a.B > 1 ? 1 : 0;
   p.n_s1 = a.Is > 0 ? (a.Is + NTS1 - 1) / NTS1 : 0;
   p.T1 = (a.I + NT1 - 1) / NT1;
-  p.T2 = (a.H + NT2 - 1) / NT2;
-  p.n_s2 = a.Is > 0 ? p.T2 * SUB2 : 0;
+  p.n_s2 = a.Is > 0 ? (a.H + NTS2 - 1) / NTS2 : 0;
+  p.n_r2 = (a.H + NTR2 - 1) / NTR2;
+  p.n_tile = (a.H + NT2 - 1) / NT2;
+  p.n_front = p.n_rt + p.n_ro + p.n_sch + p.n_s1;
   p.lds_h_off = sh.lds_h_off;
   p.lds_sched_off = sh.lds_sched_off;
-// top-k keys per lane in the first selection phase: E <= 1024 -> 4, else 16
+  // top-k keys per lane in the first selection phase: E <= 1024 -> 4, else 16
   if (a.E <= 1024) {
     if (sh.rg == 1) return sh.full ? launch_t<1, true, 4>(p, sh.lds, s) : launch_t<1, false, 4>(p, sh.lds, s);
     return sh.full ? launch_t<4, true, 4>(p, sh.lds, s) : launch_t<4, false, 4>(p, sh.lds, s);
@@ -1089,7 +1119,5 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   if (sh.rg == 1) return sh.full ? launch_t<1, true, 16>(p, sh.lds, s) : launch_t<1, false, 16>(p, sh.lds, s);
   return sh.full ? launch_t<4, true, 16>(p, sh.lds, s) : launch_t<4, false, 16>(p, sh.lds, s);
 }
-
-int layer_tiles_fc2(int H) { return (H + NT2 - 1) / NT2; }
 
 }  // namespace moe

@@ -96,112 +96,177 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ l, int E, int
   }
 }
 
-// ---------------------------------------------------------------------------
-// Workgroup top-k of one row (4 waves), for the fused layer kernel.
-//   phase 1: wave w takes the order keys of experts [w*Q, (w+1)*Q), Q =
-//            ceil(E/4), at most TPL per lane; every lane sorts its keys by
-//            (key desc, index asc); k rounds pick the wave's best remaining
-//            head (DPP max of the heads; ties -- rare -- broken by a DPP min
-//            of the tied heads' indices) and pop it -> 4 lists of <= k
-//            candidates in LDS;
-//   phase 2: wave 0 repeats the same rounds over the <= 4k candidates.
-// The k experts found are exactly those of (logit desc, index asc) order
-// over all E (the global top-k is contained in the union of the four
-// per-quarter top-k lists).  Requires E <= 256*TPL and k <= 64.
-// cand: LDS, 640 words.  Writes idx/gate (coherent) from wave 0, and returns
-// slot j's expert index to lane j of wave 0.
-// ---------------------------------------------------------------------------
-template <int TPL>
-__device__ __forceinline__ void wave_select_sorted(uint32_t (&key)[TPL], uint32_t (&ix)[TPL], int k,
-                                                   uint32_t* out_key, uint32_t* out_ix) {
-  const int lane = threadIdx.x & 63;
-  // sort this lane's TPL entries by (key desc, index asc): insertion network
+// Tagged 8-byte pairs (32-bit value | 32-bit tag << 32): data handed between
+// workgroups of one launch, polled by the consumer until its tag matches.
+__device__ __forceinline__ uint64_t make_pair(uint32_t v, uint32_t tag) { return ((uint64_t)tag << 32) | v; }
+__device__ __forceinline__ bool pair_has(uint64_t v, uint32_t tag) { return (uint32_t)(v >> 32) == tag; }
+__device__ __forceinline__ float pair_f32(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ uint64_t ld_pair(const uint64_t* p) { return ld_coh(p); }
+__device__ __forceinline__ void st_pair_f32(uint64_t* p, float v, uint32_t tag) {
+  st_coh(p, make_pair(__float_as_uint(v), tag));
+}
+
+// Polls until all `n` (<= N) pairs at p[idx(i)] carry `tag`.  Bounded: gives
+// up (returns false) after `limit` tries, or early once the sticky error word
+// *err is set (another wait of the launch already gave up).  Per-thread: no
+// barrier.
+template <int N, class Idx>
+__device__ __forceinline__ bool poll_pairs(const uint64_t* p, int n, Idx idx, uint32_t tag, uint64_t (&v)[N],
+                                           unsigned limit, const unsigned* err) {
+  for (unsigned it = 0;; ++it) {
 #pragma unroll
-  for (int i = 1; i < TPL; ++i)
+    for (int i = 0; i < N; ++i) v[i] = ld_pair(p + idx(min(i, n - 1)));
+    bool ok = true;
 #pragma unroll
-    for (int j = i; j > 0; --j) {
-      const bool sw = key[j] > key[j - 1] || (key[j] == key[j - 1] && ix[j] < ix[j - 1]);
-      const uint32_t k0 = key[j - 1], k1 = key[j], i0 = ix[j - 1], i1 = ix[j];
-      key[j - 1] = sw ? k1 : k0;
-      key[j] = sw ? k0 : k1;
-      ix[j - 1] = sw ? i1 : i0;
-      ix[j] = sw ? i0 : i1;
-    }
-  for (int j = 0; j < k; ++j) {
-    const uint32_t M = wave_max_u32(key[0]);
-    const uint64_t tied = __ballot(key[0] == M);
-    int win;
-    if (__popcll(tied) == 1) {
-      win = __ffsll((long long)tied) - 1;
-    } else {
-      const uint32_t emin = wave_min_u32(key[0] == M ? ix[0] : 0xFFFFFFFFu);
-      win = __ffsll((long long)__ballot(key[0] == M && ix[0] == emin)) - 1;
-    }
-    const uint32_t wix = (uint32_t)__builtin_amdgcn_readlane((int)ix[0], win);
-    if (lane == 0) {
-      out_key[j] = M;
-      out_ix[j] = wix;
-    }
-    if (lane == win) {  // pop the winner's head
-#pragma unroll
-      for (int i = 0; i + 1 < TPL; ++i) {
-        key[i] = key[i + 1];
-        ix[i] = ix[i + 1];
-      }
-      key[TPL - 1] = 0u;
-      ix[TPL - 1] = 0xFFFFFFFFu;
-    }
+    for (int i = 0; i < N; ++i) ok &= (i >= n) || pair_has(v[i], tag);
+    if (ok) return true;
+    if (it >= limit || ((it & 255) == 255 && ld_coh(err) != 0u)) return false;
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
+// ---------------------------------------------------------------------------
+// Workgroup top-k of one row (4 waves), for the fused layer kernel.  Order:
+// (key desc, index asc) on order-preserving integer keys, so ties go to the
+// lower expert index.  No serial k-round tournament: every step is a short
+// loop of independent compares.
+//   1. wave w holds experts [w Q, (w+1) Q), Q = ceil(E/4), <= TPL per lane;
+//      each lane takes the best of its own entries;
+//   2. the wave ranks its 64 lane-bests (each against all 64) and takes T_w
+//      = the k-th best of them.  At most k-1 entries of the wave beat T_w, so
+//      T_w is no better than the wave's k-th best entry, which in turn is no
+//      better than the row's k-th best.  Hence T = the best of the four T_w
+//      is also no better than the row's k-th best: keeping only entries at
+//      least as good as T loses none of the row's top k (at most
+//      4 ((k-1) TPL + 1) entries survive; typically a few more than k);
+//   3. survivors are compacted into LDS (ballot + prefix count + one LDS
+//      atomic per wave);
+//   4. every survivor is ranked against all survivors; rank j < k is slot j.
+// LDS `cand`: topk_lds_words(TPL) 32-bit words.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool beats(uint32_t ka, uint32_t ia, uint32_t kb, uint32_t ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__host__ __device__ constexpr int topk_lds_words(int tpl) { return 4 * 64 * tpl * 2 + 8 + 1 + 2 * 64; }
+
+// dry: one pass over whatever the logits hold, no outputs -- run while the
+// router is still working, it brings this code into the instruction cache so
+// the real pass does not stall on cold instruction fetches.
 template <int TPL>
-__device__ __forceinline__ int topk_row_wg(const float* __restrict__ l, int E, int k, uint32_t* cand,
-                                           int32_t* __restrict__ idx_out, float* __restrict__ gate_out) {
+__device__ __forceinline__ bool topk_row_wg(const uint64_t* __restrict__ l, int E, int k, uint32_t tag,
+                                            unsigned limit, const unsigned* err, uint32_t* cand,
+                                            int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+                                            uint64_t* idx_p, uint64_t* gate_p, bool dry) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int Q = (E + 3) / 4, e0 = w * Q, e1 = min(E, e0 + Q);
-  const int kw = min(k, max(e1 - e0, 0));
-  uint32_t* ck = cand + w * 64;        // wave w's candidate keys  [64]
-  uint32_t* cx = cand + 256 + w * 64;  // and expert indices       [64]
+  uint32_t* surv = cand;                      // [4 * 64 TPL] (key, index) pairs
+  uint32_t* thr = cand + 4 * 64 * TPL * 2;    // [4] (key, index) threshold of each wave
+  uint32_t* nsurv = thr + 8;                  // survivor count
+  uint32_t* out = nsurv + 1;                  // [64] (key, index) of slots 0..63
+  if (threadIdx.x == 0) *nsurv = 0u;
+  bool ok;
+  uint32_t key[TPL], ix[TPL];
   {
-    uint32_t key[TPL], ix[TPL];
-    float lv[TPL];
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) lv[i] = ld_coh(l + min(e0 + lane + 64 * i, E - 1));
+    uint64_t lv[TPL];
+    const int mine = max(0, min(TPL, (e1 - e0 - lane + 63) / 64));
+    ok = poll_pairs<TPL>(l, max(mine, 1), [&](int i) { return min(e0 + lane + 64 * i, E - 1); }, tag, lv,
+                         dry ? 0u : limit, err) || dry;
+    uint32_t bk = 0u, bi = 0xFFFFFFFFu;  // this lane's best (key 0 = no entry)
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       const int e = e0 + lane + 64 * i;
-      key[i] = e < e1 ? order_key(lv[i]) : 0u;
+      key[i] = e < e1 ? order_key(pair_f32(lv[i])) : 0u;
       ix[i] = e < e1 ? (uint32_t)e : 0xFFFFFFFFu;
+      if (key[i] != 0u && beats(key[i], ix[i], bk, bi)) {
+        bk = key[i];
+        bi = ix[i];
+      }
     }
-    if (kw > 0) wave_select_sorted<TPL>(key, ix, kw, ck, cx);
-    for (int j = kw + lane; j < 64; j += 64) {  // unused candidate slots
-      ck[j] = 0u;
-      cx[j] = 0xFFFFFFFFu;
+    // rank of this lane's best among the wave's 64 lane-bests
+    int r = 0;
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)bk, j);
+      const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)bi, j);
+      r += beats(kj, ij, bk, bi) ? 1 : 0;
+    }
+    const uint64_t th = __ballot(bk != 0u && r == k - 1);
+    uint32_t tk = 0u, ti = 0xFFFFFFFFu;  // no threshold: fewer than k lanes hold entries
+    if (th != 0ull) {
+      const int tl = __ffsll((long long)th) - 1;
+      tk = (uint32_t)__builtin_amdgcn_readlane((int)bk, tl);
+      ti = (uint32_t)__builtin_amdgcn_readlane((int)bi, tl);
+    }
+    if (lane == 0) {
+      thr[2 * w] = tk;
+      thr[2 * w + 1] = ti;
+    }
+  }
+  __syncthreads();
+  uint32_t tk = thr[0], ti = thr[1];
+#pragma unroll
+  for (int v = 1; v < 4; ++v)
+    if (beats(thr[2 * v], thr[2 * v + 1], tk, ti)) {
+      tk = thr[2 * v];
+      ti = thr[2 * v + 1];
+    }
+  {
+    bool keep[TPL];
+    uint32_t n = 0;
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      keep[i] = key[i] != 0u && !beats(tk, ti, key[i], ix[i]);
+      n += (uint32_t)__popcll(__ballot(keep[i]));
+    }
+    uint32_t base = 0;
+    if (lane == 0 && n > 0) base = atomicAdd(nsurv, n);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      const uint64_t m = __ballot(keep[i]);
+      const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (keep[i]) {
+        surv[2 * pos] = key[i];
+        surv[2 * pos + 1] = ix[i];
+      }
+      base += (uint32_t)__popcll(m);
+    }
+  }
+  __syncthreads();
+  // rank every survivor against all survivors (broadcast LDS reads, 4 per batch)
+  const uint32_t n = *nsurv;
+  for (uint32_t t = threadIdx.x; t < n; t += 256) {
+    const uint32_t mk = surv[2 * t], mi = surv[2 * t + 1];
+    int r = 0;
+    uint32_t j = 0;
+    for (; j + 4 <= n; j += 4) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(surv + 2 * j);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(surv + 2 * j + 4);
+      r += (beats(a[0], a[1], mk, mi) ? 1 : 0) + (beats(a[2], a[3], mk, mi) ? 1 : 0) +
+           (beats(b[0], b[1], mk, mi) ? 1 : 0) + (beats(b[2], b[3], mk, mi) ? 1 : 0);
+    }
+    for (; j < n; ++j) r += beats(surv[2 * j], surv[2 * j + 1], mk, mi) ? 1 : 0;
+    if (r < k) {
+      out[2 * r] = mk;
+      out[2 * r + 1] = mi;
     }
   }
   __syncthreads();
   if (w == 0) {
-    uint32_t key[4], ix[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      key[i] = cand[i * 64 + lane];
-      ix[i] = cand[256 + i * 64 + lane];
-    }
-    uint32_t* fk = cand + 512;  // final keys [64]
-    uint32_t* fx = cand + 576;  // final indices [64]
-    wave_select_sorted<4>(key, ix, k, fk, fx);
-    // lane j < k holds slot j (LDS written by lane 0 of this same wave)
-    const uint32_t myk = lane < k ? fk[lane] : 0u, myx = lane < k ? fx[lane] : 0u;
-    const float l0 = order_value(fk[0]);
+    const uint32_t myk = lane < k ? out[2 * lane] : 0u, myx = lane < k ? out[2 * lane + 1] : 0u;
+    const float l0 = order_value(out[0]);
     const float num = (lane < k) ? expf(order_value(myk) - l0) : 0.0f;
     const float den = sum_lanes<64>(num);
-    if (lane < k) {
-      st_coh(idx_out + lane, (int32_t)myx);
-      st_coh(gate_out + lane, num / den);
+    if (lane < k && !dry) {
+      const float g = num / den;
+      idx_out[lane] = (int32_t)myx;
+      gate_out[lane] = g;
+      st_coh(idx_p + lane, make_pair(myx, tag));
+      st_pair_f32(gate_p + lane, g, tag);
     }
-    return (int)myx;
   }
-  return 0;
+  return ok;
 }
 
 // ---------------------------------------------------------------------------

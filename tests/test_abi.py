@@ -56,7 +56,8 @@ class FakeTensor:
 def _weights(**over):
     base = dict(hidden=7168, inter=1536, num_experts=896, top_k=16, shared_inter=1536,
                 router_w=FakeTensor(0x10000), experts=FakeTensor(0x20000), router_bias=None,
-                shared_gate=FakeTensor(0x30000), shared_up=FakeTensor(0x40000), shared_down=FakeTensor(0x50000))
+                shared_gate=FakeTensor(0x30000), shared_up=FakeTensor(0x40000), shared_down=FakeTensor(0x50000),
+                expert_layout=moe.MOE_EXPERTS_PACKED)
     base.update(over)
     return moe.LayerWeights(**base)
 
@@ -82,6 +83,7 @@ def test_workspace_size_and_argument_errors():
         (_weights(experts=FakeTensor(0x20010)), 1),  # blob base not 256-aligned
         (_weights(shared_down=FakeTensor(0)), 1),   # partial shared expert
         (_weights(shared_inter=0), 1),              # Is == 0 but pointers given
+        (_weights(expert_layout=2), 1),             # unknown expert layout
     ]
     for w, b in bad:
         assert _ws_status(w, b)[0] == moe.MOE_ERR_INVALID_ARGUMENT, (w, b)
@@ -102,6 +104,16 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.moe_decode_layer(ctypes.byref(cs), x, r, 1, i, g, ws, 16, None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
     # misaligned workspace
     assert lib.moe_decode_layer(ctypes.byref(cs), x, r, 1, i, g, P(0x100010), 1 << 30, None) == -1
+    # the layer streams packed experts only
+    cs_canon = _weights(expert_layout=moe.MOE_EXPERTS_CANONICAL).c_struct()
+    assert lib.moe_decode_layer(ctypes.byref(cs_canon), x, r, 1, i, g, ws, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+    # pack/unpack: NULL, bad shapes, short or overlapping scratch
+    nb = moe.expert_bytes(7168, 1536)
+    assert lib.moe_pack_experts(None, 2, 7168, 1536, P(0x100000000), nb, None) == -1
+    assert lib.moe_pack_experts(P(0x200000000), 2, 7000, 1536, P(0x100000000), nb, None) == -1
+    assert lib.moe_unpack_experts(P(0x200000000), 0, 7168, 1536, P(0x100000000), nb, None) == -1
+    assert lib.moe_pack_experts(P(0x200000000), 2, 7168, 1536, P(0x100000000), nb - 1, None) == -3
+    assert lib.moe_pack_experts(P(0x200000000), 2, 7168, 1536, P(0x200000000 + nb), nb, None) == -1
     # router_topk: k > E, batch 0, H % 32
     assert lib.router_topk(x, 1, 7168, P(0x5000), None, 8, 9, i, g, P(0x6000), None, 0, None) == -1
     assert lib.router_topk(x, 0, 7168, P(0x5000), None, 896, 16, i, g, P(0x6000), None, 0, None) == -1

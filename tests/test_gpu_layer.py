@@ -168,7 +168,9 @@ def test_nan_scale_poisons_only_its_outputs():
     nb = synth.expert_bytes(cfg.hidden, cfg.inter)
     off = synth.expert_offsets(cfg.hidden, cfg.inter)
     m = 17  # down-projection row m, block 0
+    moe.unpack_experts(w.experts, w.num_experts, cfg.hidden, cfg.inter)  # edit the canonical bytes
     w.experts[e * nb + off[5] + m * (cfg.inter // 32)] = 255
+    moe.pack_experts(w.experts, w.num_experts, cfg.hidden, cfg.inter)
     out2, idx2, _ = _run_layer(w, x, res)
     assert np.array_equal(idx2, idx)
     assert np.isnan(out2[0, m])
