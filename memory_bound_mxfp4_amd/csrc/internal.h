@@ -24,7 +24,10 @@ BlobLayout blob_layout(int H, int I);
 //   active[U]         the U distinct experts any row selected, ascending
 //   row_off[U+1]      rows of active expert a are rows[row_off[a] .. row_off[a+1])
 //   rows[B*k]         slot ids s = b * k + j
+//   cg_off[U+1]       batch > 1: active expert a has column groups (up to 16
+//                     of its rows each) cg_off[a] .. cg_off[a+1]
 struct Sched {
+  int* cg_off;
   int* active;
   int* row_off;
   int* rows;
@@ -59,6 +62,8 @@ struct Workspace {
   uint64_t* hr_p;      // [B*k][I]    routed SwiGLU output, by slot
   uint64_t* os_p;      // [B][H]      shared-expert output
   uint64_t* or_p;      // [B*k][H]    routed expert outputs, by slot
+  uint64_t* hflag;     // batch > 1: [umax + 1][4][hflag_tiles] "FC1 tile done" tags
+  int hflag_tiles;
   size_t bytes;
 };
 Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B);

@@ -79,6 +79,9 @@ struct LayerParams {
   int* active;
   int* row_off;
   int* rows;
+  int* cg_off;
+  uint64_t* hflag;
+  int hflag_tiles;
   uint64_t* hs_p;
   uint64_t* hr_p;
   uint64_t* os_p;
@@ -95,6 +98,10 @@ struct LayerParams {
   int n_s2;      // shared FC2 units
   int n_r2;      // routed FC2 units per expert
   int n_tile;    // combine tiles over H
+  int mf_t1;     // batch > 1: routed FC1 units per column group (64 rows of I each)
+  int mf_t1s;    // batch > 1: shared FC1 units per column group (64 rows of Is each)
+  int mf_t2;     // batch > 1: FC2 units per column group (128 rows of H each)
+  int mf_cgs;    // batch > 1: shared-expert column groups (16 batch rows each)
   int n_front;   // units before the routed ones (router .. shared FC1)
   int n_static;  // units 0 .. n_static-1 go to workgroups 0 .. n_static-1
   int xstride;        // LDS x row stride, 16-byte granules (multiple of 8)
@@ -114,7 +121,7 @@ struct Lds {  // static LDS of the kernel
   int flag;        // "this workgroup is the last arriver"
   unsigned tag;    // this call's pair tag
   int U;           // distinct experts (once known)
-  int wtot[8];     // scan scratch
+  int wtot[12];    // scan scratch
   int nrows;       // rows of the current unit
   double part[4][4];  // router: partial sums of the second half-row waves [wave][row]
   float gates[MOE_MAX_TOPK];  // combine: gates of the current row
@@ -130,6 +137,7 @@ struct WgState {
   const int* s_active;   // LDS copy of the schedule (valid once route_seen)
   const int* s_row_off;
   const int* s_rows;
+  const int* s_cg_off;
 };
 
 // Bounded poll of one control word until it has `tag` in its high half
@@ -157,6 +165,7 @@ __device__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* s
   int* a = sc;
   int* ro = sc + p.umax;
   int* rw = ro + p.umax + 1;
+  int* cgo = rw + p.B * p.k;
   if (p.B == 1) {
     if (threadIdx.x < p.k) {
       uint64_t v[1];
@@ -174,14 +183,16 @@ __device__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* s
     if (threadIdx.x == 0) L.U = (int)min(poll_ready(p, st.tag), (uint32_t)p.umax);
     __syncthreads();
     const int U = L.U, nslots = p.B * p.k;
-    const int total = U + (U + 1) + nslots;
+    const int total = U + (U + 1) + nslots + (U + 1);
     for (int base = threadIdx.x; base < total; base += 256 * 8) {
       int v[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int i = min(base + 256 * t, total - 1);
         v[t] = i < U ? ld_coh(p.active + i)
-                     : (i < 2 * U + 1 ? ld_coh(p.row_off + (i - U)) : ld_coh(p.rows + (i - 2 * U - 1)));
+                     : (i < 2 * U + 1 ? ld_coh(p.row_off + (i - U))
+                                      : (i < 2 * U + 1 + nslots ? ld_coh(p.rows + (i - 2 * U - 1))
+                                                                : ld_coh(p.cg_off + (i - 2 * U - 1 - nslots))));
       }
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -189,7 +200,8 @@ __device__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* s
         if (i < total) {
           if (i < U) a[i] = v[t];
           else if (i < 2 * U + 1) ro[i - U] = v[t];
-          else rw[i - 2 * U - 1] = v[t];
+          else if (i < 2 * U + 1 + nslots) rw[i - 2 * U - 1] = v[t];
+          else cgo[i - 2 * U - 1 - nslots] = v[t];
         }
       }
     }
@@ -199,6 +211,7 @@ __device__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* s
   st.s_active = a;
   st.s_row_off = ro;
   st.s_rows = rw;
+  st.s_cg_off = cgo;
   st.route_seen = true;
 }
 
@@ -648,35 +661,39 @@ __device__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt
   for (int s = t; s < nslots; s += 256) atomicAdd(&cnt[ids[s]], 1);
   __syncthreads();
   const int per = (p.E + 255) / 256, e0 = t * per;
-  int run_rows = 0, run_act = 0;
+  int run_rows = 0, run_act = 0, run_cg = 0;  // rows, active experts, column groups
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e < p.E) {
       run_rows += cnt[e];
       run_act += cnt[e] > 0;
+      run_cg += (cnt[e] + 15) >> 4;
     }
   }
   const int lane = t & 63, w = t >> 6;
-  int ir = run_rows, ia = run_act;
+  int ir = run_rows, ia = run_act, ic = run_cg;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int vr = __shfl_up(ir, d, 64), va = __shfl_up(ia, d, 64);
+    const int vr = __shfl_up(ir, d, 64), va = __shfl_up(ia, d, 64), vc = __shfl_up(ic, d, 64);
     if (lane >= d) {
       ir += vr;
       ia += va;
+      ic += vc;
     }
   }
   if (lane == 63) {
     wtot[w] = ir;
     wtot[4 + w] = ia;
+    wtot[8 + w] = ic;
   }
   __syncthreads();
-  int base_r = 0, base_a = 0;
+  int base_r = 0, base_a = 0, base_c = 0;
   for (int i = 0; i < w; ++i) {
     base_r += wtot[i];
     base_a += wtot[4 + i];
+    base_c += wtot[8 + i];
   }
-  int pr = base_r + ir - run_rows, pa = base_a + ia - run_act;
+  int pr = base_r + ir - run_rows, pa = base_a + ia - run_act, pc = base_c + ic - run_cg;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e < p.E) {
@@ -684,12 +701,17 @@ __device__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt
       if (cnt[e] > 0) {
         st_coh(p.active + pa, e);
         st_coh(p.row_off + pa, pr);
+        st_coh(p.cg_off + pa, pc);
         ++pa;
       }
       pr += cnt[e];
+      pc += (cnt[e] + 15) >> 4;
     }
   }
-  if (t == 255) st_coh(p.row_off + base_a + ia, base_r + ir);
+  if (t == 255) {
+    st_coh(p.row_off + base_a + ia, base_r + ir);
+    st_coh(p.cg_off + base_a + ia, base_c + ic);
+  }
   __syncthreads();
   for (int s = t; s < nslots; s += 256) {
     const int pos = atomicAdd(&start[ids[s]], 1);
@@ -933,6 +955,380 @@ __device__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, i
   p.residual[(size_t)b * p.H + m] = acc;
 }
 
+// ---- MFMA path (batch > 1) ----------------------------------------------------
+//
+// With more than one activation row per expert the contraction is dense
+// enough for the matrix cores: an expert's rows are taken 16 at a time (a
+// "column group"), and every 16x16x32 bf16 MFMA multiplies 16 weight rows x
+// 32 elements (A) by 32 elements x 16 activation rows (B) into fp32.
+//   * A: the packed MXFP4 tiles already hold what a lane needs -- lane
+//     l = 16 q + r has, in slab kb, block 4 kb + q of row r (32 elements);
+//     dword d of it is exactly the 8 elements of its k-slot for MFMA (kb, d),
+//     decoded to bf16 exactly by the scaled conversion.  The bf16 shared
+//     expert is read in place (lane l: 8 elements of row r at 32 j + 8 q).
+//   * B: activations for a K segment are staged in LDS as [16 columns][KS]
+//     bf16 (row stride KS*2 + 16 bytes, so the 16 lanes of a k-slot hit
+//     distinct banks); lane l reads column r, the 8 elements of its k-slot.
+//     FC2's fp32 h is split into bf16 hi + lo (two MFMAs), which keeps the
+//     product within ~2^-17 of the fp32 one.
+//   * D: lane l holds rows 4 q .. 4 q + 3 of the tile for column r.
+// FC1 stages x segments double-buffered (one barrier per segment); FC2
+// stages h per segment after a barrier.  An FC1 unit publishes "tile done"
+// (a tagged flag, after its h stores have completed); FC2 units of that
+// column group wait for all of its FC1 tiles, then read plain fp32 h.
+constexpr int MF_COLS = 16;   // activation rows per column group
+constexpr int MF_NT1 = 64;    // FC1 rows per unit: one 16-row group per wave
+constexpr int MF_NT2 = 128;   // FC2 rows per unit: two 16-row groups per wave
+constexpr int MF_XS_FP4 = 512 * 2 + 16;  // LDS column stride (bytes) of a 512-element segment
+constexpr int MF_XS_BF = 128 * 2 + 16;   // ... of a 128-element segment (bf16 weights)
+
+__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float s) {
+  bf16x2 t[4];
+  dq4_bf16(w, s, t);
+  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, t[0]), __builtin_bit_cast(uint32_t, t[1]),
+                                          __builtin_bit_cast(uint32_t, t[2]), __builtin_bit_cast(uint32_t, t[3])});
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Column list of a unit: batch rows 16 cg .. of the shared expert (a < 0),
+// or rows 16 cg .. of active expert a's row list (slot ids).
+__device__ __forceinline__ void load_cols(const LayerParams& p, const WgState& st, Lds& L, int a, int cg) {
+  __syncthreads();
+  if (a < 0) {
+    const int n = min(MF_COLS, p.B - MF_COLS * cg);
+    if ((int)threadIdx.x < n) L.slot[threadIdx.x] = MF_COLS * cg + threadIdx.x;
+    if (threadIdx.x == 0) L.nrows = n;
+  } else {
+    const int r0 = st.s_row_off[a] + MF_COLS * cg, n = min(MF_COLS, st.s_row_off[a + 1] - r0);
+    if ((int)threadIdx.x < n) L.slot[threadIdx.x] = st.s_rows[r0 + threadIdx.x];
+    if (threadIdx.x == 0) L.nrows = n;
+  }
+  __syncthreads();
+}
+
+// (active expert, column group) of global column group gc (binary search of
+// the LDS copy of cg_off).
+__device__ __forceinline__ int find_expert(const WgState& st, int gc) {
+  int lo = 0, hi = st.U - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (st.s_cg_off[mid] <= gc) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ uint64_t* hflag_at(const LayerParams& p, int ex /* umax = shared */, int cg, int t) {
+  return p.hflag + ((size_t)ex * 4 + cg) * p.hflag_tiles + t;
+}
+
+// x segment [s*KS, s*KS + KS) of the unit's columns into registers (16 B per
+// chunk; NCH chunks per thread), zero for absent columns and beyond H.
+template <int KS>
+struct XSeg {
+  static constexpr int NCH = MF_COLS * KS * 2 / 16 / 256;  // 16-byte chunks per thread
+  u32x4 v[NCH];
+  __device__ void load(const LayerParams& p, const Lds& L, bool routed, int s, int nc) {
+    constexpr int CPC = KS * 2 / 16;  // chunks per column
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + 256 * i, c = ch / CPC, j = ch - c * CPC;
+      const int k0 = s * KS + 8 * j;
+      const bool ok = c < nc && k0 < p.H;
+      const int b = ok ? (routed ? L.slot[c] / p.k : L.slot[c]) : 0;
+      v[i] = ok ? *reinterpret_cast<const u32x4*>(p.x + (size_t)b * p.H + k0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ void store(char* buf) const {
+    constexpr int CPC = KS * 2 / 16, XS = KS * 2 + 16;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + 256 * i, c = ch / CPC, j = ch - c * CPC;
+      *reinterpret_cast<u32x4*>(buf + c * XS + 16 * j) = v[i];
+    }
+  }
+};
+
+// One FC1 segment of a wave: gate and up A-operand data.
+//   FP4:  q[m][kb] = packed slab kb of the gate (m 0) / up (m 1) tile; s[m] its scales
+//   bf16: q[m][j]  = 8 elements of row r at s*128 + 32 j + 8 q
+struct MfBuf {
+  u32x4 q[2][4];
+  u32x4 s[2];
+};
+
+template <bool FP4, bool FULL>
+__device__ __forceinline__ void mf1_load(const LayerParams& p, const uint8_t* blob, int g, int s, MfBuf& b, float dep) {
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  if (FP4) {
+    const int C1 = p.H / 32;
+    const int SC = FULL ? 16 : min(16, C1 - 16 * s);
+    const uint8_t* gt = blob + 2 * tile_off(g, s, C1) + after(0, dep);
+    load_tile<FULL>(gt, SC, b.q[0], b.s[0]);
+    load_tile<FULL>(gt + SC * 272, SC, b.q[1], b.s[1]);
+  } else {
+    const int n = min(16 * g + r, p.Is - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = min(s * 128 + 32 * j + 8 * q, p.H - 8) + after(0, dep);
+      b.q[0][j] = ld_weight16(p.sg + (size_t)n * p.H + k0);
+      b.q[1][j] = ld_weight16(p.su + (size_t)n * p.H + k0);
+    }
+  }
+}
+
+template <bool FP4, bool FULL>
+__device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBuf& b, const char* xb, f32x4& ag,
+                                         f32x4& au) {
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  if (FP4) {
+    const int C1 = p.H / 32;
+    const int SC = FULL ? 16 : min(16, C1 - 16 * s);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int c = 4 * kb + q;
+      const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
+      const float sg = e8m0_scale(tile_scale<FULL>(b.s[0], kb, q));
+      const float su = e8m0_scale(tile_scale<FULL>(b.s[1], kb, q));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xb + after(r * MF_XS_FP4 + (128 * kb + 32 * q + 8 * d) * 2, ag[0]));
+        ag = mfma_bf16(fp4x8_bf16(b.q[0][kb][d] & msk, sg), xv, ag);
+        au = mfma_bf16(fp4x8_bf16(b.q[1][kb][d] & msk, su), xv, au);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = s * 128 + 32 * j + 8 * q < p.H;
+      const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xb + r * MF_XS_BF + (32 * j + 8 * q) * 2);
+      const u32x4 z{0u, 0u, 0u, 0u};
+      ag = mfma_bf16(__builtin_bit_cast(bf16x8, ok ? b.q[0][j] : z), xv, ag);
+      au = mfma_bf16(__builtin_bit_cast(bf16x8, ok ? b.q[1][j] : z), xv, au);
+    }
+  }
+}
+
+// FC1 + SwiGLU of rows [64 t, 64 t + 64) (wave w: row group 4 t + w) of the
+// routed expert a (FP4) or the shared expert (bf16, a < 0), column group cg.
+template <bool FP4, bool FULL>
+__device__ void mf_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
+  constexpr int KS = FP4 ? 512 : 128, XS = KS * 2 + 16;
+  load_cols(p, st, L, a, cg);
+  const int nc = L.nrows;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int N = FP4 ? p.I : p.Is;
+  const int g = 4 * t + w;
+  const uint8_t* blob = FP4 ? p.experts + (size_t)st.s_active[a] * p.blob_bytes : nullptr;
+  const int S = FP4 ? (p.H / 32 + 15) / 16 : (p.H + 127) / 128;
+  const int gl = min(g, (N + 15) / 16 - 1);  // waves past the last row group load a valid group, store nothing
+  f32x4 ag{0.f, 0.f, 0.f, 0.f}, au{0.f, 0.f, 0.f, 0.f};
+  MfBuf ba, bb;
+  mf1_load<FP4, FULL>(p, blob, gl, 0, ba, 0.f);
+  if (S > 1) mf1_load<FP4, FULL>(p, blob, gl, 1, bb, 0.f);
+  {
+    XSeg<KS> x0;
+    x0.load(p, L, a >= 0, 0, nc);
+    x0.store(mfb);
+  }
+  __syncthreads();
+  for (int s = 0; s < S; s += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ss = s + h;
+      if (ss < S) {
+        XSeg<KS> xn;
+        if (ss + 1 < S) xn.load(p, L, a >= 0, ss + 1, nc);
+        MfBuf& b = h ? bb : ba;
+        mf1_math<FP4, FULL>(p, ss, b, mfb + (ss & 1) * MF_COLS * XS, ag, au);
+        if (ss + 2 < S) mf1_load<FP4, FULL>(p, blob, gl, ss + 2, b, ag[0] + au[0]);
+        if (ss + 1 < S) xn.store(mfb + ((ss + 1) & 1) * MF_COLS * XS);
+        __syncthreads();
+      }
+    }
+  }
+  // h = silu(gate) * up: rows 16 g + 4 q + i of column r, as fp32 (two 8-byte coherent stores)
+  float* hout = FP4 ? reinterpret_cast<float*>(p.hr_p) : reinterpret_cast<float*>(p.hs_p);
+  const int n0 = 16 * g + 4 * q;
+  if (n0 < N && r < nc) {  // N is a multiple of 8: rows n0 .. n0+3 all exist
+    float hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = silu_f(ag[i]) * au[i];
+    uint64_t* dst = reinterpret_cast<uint64_t*>(hout + (size_t)L.slot[r] * N + n0);
+    st_coh(dst, ((uint64_t)__float_as_uint(hv[1]) << 32) | __float_as_uint(hv[0]));
+    st_coh(dst + 1, ((uint64_t)__float_as_uint(hv[3]) << 32) | __float_as_uint(hv[2]));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every lane's h stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) st_coh(hflag_at(p, a < 0 ? p.umax : a, cg, t), make_pair(1u, st.tag));
+}
+
+// One FC2 segment of a wave: two 16-row A tiles of the down matrix.
+//   FP4:  q[t][kb] = packed slab kb of tile t, s[t] its scales
+//   bf16: q[t][j]  = 8 elements of row r of tile t at s*128 + 32 j + 8 q
+template <bool FP4, bool FULL>
+__device__ __forceinline__ void mf2_load(const LayerParams& p, const uint8_t* down, const int (&gt)[2], int s,
+                                         MfBuf& b, float dep) {
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  if (FP4) {
+    const int C2 = p.I / 32;
+    const int SC = FULL ? 16 : min(16, C2 - 16 * s);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) load_tile<FULL>(down + tile_off(gt[t], s, C2) + after(0, dep), SC, b.q[t], b.s[t]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int m = min(16 * gt[t] + r, p.H - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k0 = min(s * 128 + 32 * j + 8 * q, p.Is - 8) + after(0, dep);
+        b.q[t][j] = ld_weight16(p.sd + (size_t)m * p.Is + k0);
+      }
+    }
+  }
+}
+
+template <bool FP4, bool FULL>
+__device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBuf& b, const char* hb, f32x4 (&acc)[2]) {
+  constexpr int KS = FP4 ? 512 : 128, XS = KS * 2 + 16;
+  const char* lob = hb + MF_COLS * XS;  // lo halves follow the hi halves
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  if (FP4) {
+    const int C2 = p.I / 32;
+    const int SC = FULL ? 16 : min(16, C2 - 16 * s);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int c = 4 * kb + q;
+      const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
+      float sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sc[t] = e8m0_scale(tile_scale<FULL>(b.s[t], kb, q));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int off = after(r * XS + (128 * kb + 32 * q + 8 * d) * 2, acc[0][0] + acc[1][0]);
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(hb + off);
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(lob + off);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 wv = fp4x8_bf16(b.q[t][kb][d] & msk, sc[t]);
+          acc[t] = mfma_bf16(wv, hi, acc[t]);
+          acc[t] = mfma_bf16(wv, lo, acc[t]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = s * 128 + 32 * j + 8 * q < p.Is;
+      const int off = r * XS + (32 * j + 8 * q) * 2;
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(hb + off);
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(lob + off);
+      const u32x4 z{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 wv = __builtin_bit_cast(bf16x8, ok ? b.q[t][j] : z);
+        acc[t] = mfma_bf16(wv, hi, acc[t]);
+        acc[t] = mfma_bf16(wv, lo, acc[t]);
+      }
+    }
+  }
+}
+
+// h segment [s*KS, s*KS + KS) of the unit's columns (fp32, written by this
+// launch's FC1 units: 8-byte coherent loads) into LDS as bf16 hi and lo.
+template <int KS>
+__device__ __forceinline__ void mf_stage_h(const LayerParams& p, const Lds& L, const float* hsrc, int K, int s, int nc,
+                                           char* hb) {
+  constexpr int XS = KS * 2 + 16, PER = MF_COLS * KS / 2 / 256;  // 8-byte loads per thread
+  uint64_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i, c = e / (KS / 2), j = e - c * (KS / 2);
+    const int k0 = s * KS + 2 * j;
+    const bool ok = c < nc && k0 < K;
+    v[i] = ok ? __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(hsrc) + (size_t)L.slot[c] * K + k0),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+              : 0ull;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = threadIdx.x + 256 * i, c = e / (KS / 2), j = e - c * (KS / 2);
+    uint32_t hi2 = 0, lo2 = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float f = __uint_as_float((uint32_t)(v[i] >> (32 * h)));
+      const uint16_t hb16 = f32_to_bf16(f);
+      const float rem = f - __uint_as_float((uint32_t)hb16 << 16);
+      hi2 |= (uint32_t)hb16 << (16 * h);
+      lo2 |= (uint32_t)f32_to_bf16(rem) << (16 * h);
+    }
+    *reinterpret_cast<uint32_t*>(hb + c * XS + 4 * j) = hi2;
+    *reinterpret_cast<uint32_t*>(hb + MF_COLS * XS + c * XS + 4 * j) = lo2;
+  }
+}
+
+// FC2 of rows [128 t, 128 t + 128) of H (wave w: row groups 8 t + w and
+// 8 t + w + 4) of routed expert a (FP4) or the shared expert (a < 0), column
+// group cg, once every FC1 tile of that column group is done.
+template <bool FP4, bool FULL>
+__device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
+  constexpr int KS = FP4 ? 512 : 128;
+  load_cols(p, st, L, a, cg);
+  const int nc = L.nrows;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int K = FP4 ? p.I : p.Is;
+  const int G = p.H / 16;
+  const int gt[2] = {min(8 * t + w, G - 1), min(8 * t + w + 4, G - 1)};
+  const uint8_t* down =
+      FP4 ? p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * (p.H / 32) * 17 : nullptr;
+  const int S = FP4 ? (K / 32 + 15) / 16 : (K + 127) / 128;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  MfBuf ba, bb;
+  mf2_load<FP4, FULL>(p, down, gt, 0, ba, 0.f);  // the weights do not depend on FC1
+  if (S > 1) mf2_load<FP4, FULL>(p, down, gt, 1, bb, 0.f);
+  {  // wait until every FC1 tile of this column group has published its h
+    const int ntile = (K + MF_NT1 - 1) / MF_NT1;
+    bool ok = true;
+    if ((int)threadIdx.x < ntile) {
+      uint64_t f[1];
+      const int ti = threadIdx.x;
+      ok = poll_pairs<1>(hflag_at(p, a < 0 ? p.umax : a, cg, 0), 1, [&](int) { return ti; }, st.tag, f, SPIN_LIMIT,
+                         p.ctrl + CTRL_ERR);
+    }
+    if (!ok) set_error(p);
+  }
+  const float* hsrc = FP4 ? reinterpret_cast<const float*>(p.hr_p) : reinterpret_cast<const float*>(p.hs_p);
+  for (int s = 0; s < S; s += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ss = s + h;
+      if (ss < S) {
+        __syncthreads();  // the previous segment's h is no longer read
+        mf_stage_h<KS>(p, L, hsrc, K, ss, nc, mfb);
+        __syncthreads();
+        MfBuf& b = h ? bb : ba;
+        mf2_math<FP4, FULL>(p, ss, b, mfb, acc);
+        if (ss + 2 < S) mf2_load<FP4, FULL>(p, down, gt, ss + 2, b, acc[0][0] + acc[1][0]);
+      }
+    }
+  }
+  uint64_t* out = FP4 ? p.or_p : p.os_p;
+  if (r < nc) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int g = 8 * t + w + 4 * tt;
+      if (g < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st_pair_f32(out + (size_t)L.slot[r] * p.H + 16 * g + 4 * q + i, acc[tt][i], st.tag);
+      }
+    }
+  }
+}
+
 // ---- the kernel ------------------------------------------------------------------
 
 // FULL: the layer's shape makes every weight-stream segment and FC2 row group
@@ -943,6 +1339,8 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   extern __shared__ u32x4 lds_raw[];
   u32x4* xs = lds_raw;
   u32x4* hs = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(lds_raw) + p.lds_h_off);
+  constexpr bool MF = RG > 1;  // batch > 1: routed and shared experts on the matrix cores
+  char* mfb = reinterpret_cast<char*>(lds_raw);  // MFMA staging (aliases the x region: one unit at a time)
   int* sched_lds = reinterpret_cast<int*>(reinterpret_cast<char*>(lds_raw) + p.lds_sched_off);
   __shared__ Lds L;
   if (threadIdx.x == 0) {
@@ -950,7 +1348,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     L.tag = (epoch == 0xFFFFFFFFu) ? 1u : epoch + 1u;  // never 0: a cleared workspace holds no valid pair
   }
   __syncthreads();
-  WgState st{false, false, 0, L.tag, nullptr, nullptr, nullptr};
+  WgState st{false, false, 0, L.tag, nullptr, nullptr, nullptr, nullptr};
   // The first units (router, routing, shared FC1) go by workgroup index, so
   // the launch ramp does not queue on the head counter.
   int u = (int)blockIdx.x < p.n_static ? (int)blockIdx.x : -1;
@@ -973,7 +1371,8 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
       build_schedule(p, st, reinterpret_cast<int*>(xs), L.wtot);
       st.x_cached = false;
     } else if ((rel -= p.n_sch) < p.n_s1) {
-      shared_fc1_unit<RG, FULL>(p, st, L, xs, rel);
+      if constexpr (MF) mf_fc1_unit<false, FULL>(p, st, L, mfb, -1, rel / p.mf_t1s, rel % p.mf_t1s);
+      else shared_fc1_unit<RG, FULL>(p, st, L, xs, rel);
     } else {
       rel -= p.n_s1;
       if (!st.route_seen) {
@@ -981,16 +1380,33 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
         cache_schedule(p, st, L, sched_lds);
       }
       const int U = st.U;
-      if (rel < U * p.T1) {
-        routed_fc1_unit<RG, FULL>(p, st, L, xs, rel / p.T1, rel % p.T1);
-      } else if ((rel -= U * p.T1) < p.n_s2) {
-        shared_fc2_unit<RG, FULL>(p, st, L, hs, rel);
-      } else if ((rel -= p.n_s2) < U * p.n_r2) {
-        routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / p.n_r2, rel % p.n_r2);
-      } else if ((rel -= U * p.n_r2) < p.B * p.n_tile) {
-        combine_unit(p, st, L, rel / p.n_tile, rel % p.n_tile);
+      if constexpr (MF) {
+        const int NCG = st.s_cg_off[U];  // column groups of all active experts
+        if (rel < NCG * p.mf_t1) {
+          const int gc = rel / p.mf_t1, ae = find_expert(st, gc);
+          mf_fc1_unit<true, FULL>(p, st, L, mfb, ae, gc - st.s_cg_off[ae], rel % p.mf_t1);
+        } else if ((rel -= NCG * p.mf_t1) < p.n_s2) {
+          mf_fc2_unit<false, FULL>(p, st, L, mfb, -1, rel / p.mf_t2, rel % p.mf_t2);
+        } else if ((rel -= p.n_s2) < NCG * p.mf_t2) {
+          const int gc = rel / p.mf_t2, ae = find_expert(st, gc);
+          mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, gc - st.s_cg_off[ae], rel % p.mf_t2);
+        } else if ((rel -= NCG * p.mf_t2) < p.B * p.n_tile) {
+          combine_unit(p, st, L, rel / p.n_tile, rel % p.n_tile);
+        } else {
+          break;
+        }
       } else {
-        break;
+        if (rel < U * p.T1) {
+          routed_fc1_unit<RG, FULL>(p, st, L, xs, rel / p.T1, rel % p.T1);
+        } else if ((rel -= U * p.T1) < p.n_s2) {
+          shared_fc2_unit<RG, FULL>(p, st, L, hs, rel);
+        } else if ((rel -= p.n_s2) < U * p.n_r2) {
+          routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / p.n_r2, rel % p.n_r2);
+        } else if ((rel -= U * p.n_r2) < p.B * p.n_tile) {
+          combine_unit(p, st, L, rel / p.n_tile, rel % p.n_tile);
+        } else {
+          break;
+        }
       }
     }
     __syncthreads();
@@ -1028,6 +1444,7 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   // bf16 shared-expert stream segment is complete, and every unit's rows exist
   s.full = (H % 512 == 0) && (I % 512 == 0) && (H % (32 * 8 * CPL1) == 0) && (Is % (8 * 8 * CPL2) == 0) &&
            (Is % NTS1 == 0) && (H % NTR2 == 0) && (H % NTS2 == 0);
+  if (B > 1) s.full = (H % 512 == 0) && (I % 512 == 0);  // the MFMA path: every packed tile is complete
   s.xstride = ((H / 8 + 7) / 8) * 8;
   int K2 = I > Is ? I : Is;
   s.hstride = ((K2 / 4 + 7) / 8) * 8;
@@ -1036,12 +1453,17 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   // schedule's counts (2E) and slot ids (B*k)
   size_t keys_bytes = (size_t)topk_lds_words(E <= 1024 ? 4 : 16) * 4, cnt_bytes = (size_t)(2 * E + B * k) * 4;
   size_t sched_bytes = keys_bytes > cnt_bytes ? keys_bytes : cnt_bytes;
-  size_t xr = align256(x_bytes > sched_bytes ? x_bytes : sched_bytes);
+  size_t xr = x_bytes > sched_bytes ? x_bytes : sched_bytes;
+  // batch > 1: the MFMA staging buffers (two 16-column segments) alias this
+  // region, and no h rows are staged
+  const size_t mf_bytes = (size_t)2 * 16 * (512 * 2 + 16);
+  if (B > 1 && mf_bytes > xr) xr = mf_bytes;
+  xr = align256(xr);
   s.lds_h_off = (int)xr;
-  size_t hr = align256((size_t)s.rg * s.hstride * 16);
+  size_t hr = B > 1 ? 0 : align256((size_t)s.rg * s.hstride * 16);
   s.lds_sched_off = (int)(xr + hr);
   const size_t slots = (size_t)B * k, umax = slots < (size_t)E ? slots : (size_t)E;
-  s.lds = xr + hr + align256(4 * (2 * umax + 1 + slots));
+  s.lds = xr + hr + align256(4 * (3 * umax + 2 + slots));
   return s;
 }
 
@@ -1108,6 +1530,17 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.n_s2 = a.Is > 0 ? (a.H + NTS2 - 1) / NTS2 : 0;
   p.n_r2 = (a.H + NTR2 - 1) / NTR2;
   p.n_tile = (a.H + NT2 - 1) / NT2;
+  p.mf_t1 = (a.I + MF_NT1 - 1) / MF_NT1;
+  p.mf_t1s = (a.Is + MF_NT1 - 1) / MF_NT1;
+  p.mf_t2 = (a.H + MF_NT2 - 1) / MF_NT2;
+  p.mf_cgs = (a.B + MF_COLS - 1) / MF_COLS;
+  if (a.B > 1) {  // MFMA path: shared expert units per column group
+    p.n_s1 = a.Is > 0 ? p.mf_cgs * p.mf_t1s : 0;
+    p.n_s2 = a.Is > 0 ? p.mf_cgs * p.mf_t2 : 0;
+  }
+  p.cg_off = a.ws.sched.cg_off;
+  p.hflag = a.ws.hflag;
+  p.hflag_tiles = a.ws.hflag_tiles;
   p.n_front = p.n_rt + p.n_ro + p.n_sch + p.n_s1;
   p.lds_h_off = sh.lds_h_off;
   p.lds_sched_off = sh.lds_sched_off;
