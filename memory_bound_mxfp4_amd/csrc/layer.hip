@@ -751,6 +751,60 @@ __device__ void router_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs
   }
 }
 
+// Router unit at batch > 1: experts 2u' and 2u'+1 against a block of 16 rows
+// (u' = u mod pairs, block = u / pairs), so the router matrix is streamed
+// once per 16 rows.  Wave w takes expert 2u' + (w >> 1) and rows 8 (w & 1)
+// .. + 7; lane l takes 8-element chunks c = l, l + 64, ... of the row.  The
+// activation chunks are read straight from global memory: all units read
+// the same few hundred KB of x, which stays in L2, so no LDS staging or
+// barrier is needed and every wave keeps its loads in flight.  Products
+// bf16 x bf16 are exact in fp32 and are summed exactly in fp64.
+__device__ void router_mf_unit(const LayerParams& p, WgState& st, int u) {
+  constexpr int RB = 8;  // rows per wave
+  const int pe = u % p.n_rt_e, blk = u / p.n_rt_e;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = min(2 * pe + (w >> 1), p.E - 1);
+  const int b0 = 16 * blk + RB * (w & 1), nr = min(RB, p.B - b0);
+  if (nr <= 0) return;  // wave-uniform: this wave's rows are past the batch
+  const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wr + (size_t)e * p.H);
+  const u32x4* xr[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) xr[r] = reinterpret_cast<const u32x4*>(p.x + (size_t)(b0 + min(r, nr - 1)) * p.H);
+  double acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = 0.0;
+  const int C = p.H / 8;
+  for (int c = lane; c < C; c += 64) {
+    const u32x4 wv = ld_weight16(wrow + c);
+    u32x4 xv[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) xv[r] = xr[r][c];
+    float wf[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      wf[2 * d] = bf16_lo(wv[d]);
+      wf[2 * d + 1] = bf16_hi(wv[d]);
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      double a = acc[r];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        a += (double)(wf[2 * d] * bf16_lo(xv[r][d]));
+        a += (double)(wf[2 * d + 1] * bf16_hi(xv[r][d]));
+      }
+      acc[r] = a;
+    }
+  }
+  const double bb = p.bias ? (double)p.bias[e] : 0.0;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const double v = sum_lanes_f64<64>(acc[r]);
+    if (lane == 0 && r < nr && 2 * pe + (w >> 1) < p.E)
+      st_pair_f32(p.logits_p + (size_t)(b0 + r) * p.E + e, (float)(v + bb), st.tag);
+  }
+}
+
 // Routing unit of row b: top-k over the row's logits (polled until the router
 // has written them all) and the gates.  Top-k state lives in LDS (the x
 // region): holding it in registers would set the register budget -- and so
@@ -978,9 +1032,11 @@ __device__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, i
 // column group wait for all of its FC1 tiles, then read plain fp32 h.
 constexpr int MF_COLS = 16;   // activation rows per column group
 constexpr int MF_NT1 = 64;    // FC1 rows per unit: one 16-row group per wave
-constexpr int MF_NT2 = 128;   // FC2 rows per unit: two 16-row groups per wave
+constexpr int MF_MT2 = 4;     // FC2 unit: four 128-row tiles (two 16-row groups per wave each)
+constexpr int MF_NT2 = 128 * MF_MT2;  // FC2 rows of H per unit
 constexpr int MF_XS_FP4 = 512 * 2 + 16;  // LDS column stride (bytes) of a 512-element segment
 constexpr int MF_XS_BF = 128 * 2 + 16;   // ... of a 128-element segment (bf16 weights)
+constexpr int MF_STAGE_BYTES = 2 * MF_COLS * MF_XS_FP4;  // LDS staging region of the MFMA units
 
 __device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float s) {
   bf16x2 t[4];
@@ -1080,10 +1136,14 @@ __device__ __forceinline__ void mf1_load(const LayerParams& p, const uint8_t* bl
   }
 }
 
+// xb: the segment's activations for this lane's column (column stride
+// already applied); xoff: byte offset of the segment inside that column;
+// live: this lane's column exists (else its B fragment is zero).
 template <bool FP4, bool FULL>
-__device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBuf& b, const char* xb, f32x4& ag,
-                                         f32x4& au) {
-  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+__device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBuf& b, const char* xb, int xoff,
+                                         bool live, f32x4& ag, f32x4& au) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
+  const u32x4 z{0u, 0u, 0u, 0u};
   if (FP4) {
     const int C1 = p.H / 32;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
@@ -1095,7 +1155,8 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
       const float su = e8m0_scale(tile_scale<FULL>(b.s[1], kb, q));
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xb + after(r * MF_XS_FP4 + (128 * kb + 32 * q + 8 * d) * 2, ag[0]));
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(xb + after(xoff + (128 * kb + 32 * q + 8 * (FULL || c < SC ? d : 0)) * 2, ag[0]));
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, (live && (FULL || c < SC)) ? raw : z);
         ag = mfma_bf16(fp4x8_bf16(b.q[0][kb][d] & msk, sg), xv, ag);
         au = mfma_bf16(fp4x8_bf16(b.q[1][kb][d] & msk, su), xv, au);
       }
@@ -1104,8 +1165,8 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool ok = s * 128 + 32 * j + 8 * q < p.H;
-      const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xb + r * MF_XS_BF + (32 * j + 8 * q) * 2);
-      const u32x4 z{0u, 0u, 0u, 0u};
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(xb + xoff + (ok ? (32 * j + 8 * q) * 2 : 0));
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, (live && ok) ? raw : z);
       ag = mfma_bf16(__builtin_bit_cast(bf16x8, ok ? b.q[0][j] : z), xv, ag);
       au = mfma_bf16(__builtin_bit_cast(bf16x8, ok ? b.q[1][j] : z), xv, au);
     }
@@ -1129,24 +1190,57 @@ __device__ void mf_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
   MfBuf ba, bb;
   mf1_load<FP4, FULL>(p, blob, gl, 0, ba, 0.f);
   if (S > 1) mf1_load<FP4, FULL>(p, blob, gl, 1, bb, 0.f);
-  {
-    XSeg<KS> x0;
-    x0.load(p, L, a >= 0, 0, nc);
-    x0.store(mfb);
-  }
-  __syncthreads();
-  for (int s = 0; s < S; s += 2) {
+  const int XF = p.H * 2 + 16;  // column stride of whole-K staging
+  if (nc * XF <= MF_STAGE_BYTES) {
+    // Narrow column group: all of K for every column in LDS at once, then
+    // the weights stream with no barrier (the common case at small batch).
+    constexpr int PER = 8;
+    const int CPC = p.H / 8, total = nc * CPC;
+    for (int base = threadIdx.x; base < total; base += 256 * PER) {
+      u32x4 v[PER];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ss = s + h;
-      if (ss < S) {
-        XSeg<KS> xn;
-        if (ss + 1 < S) xn.load(p, L, a >= 0, ss + 1, nc);
-        MfBuf& b = h ? bb : ba;
-        mf1_math<FP4, FULL>(p, ss, b, mfb + (ss & 1) * MF_COLS * XS, ag, au);
-        if (ss + 2 < S) mf1_load<FP4, FULL>(p, blob, gl, ss + 2, b, ag[0] + au[0]);
-        if (ss + 1 < S) xn.store(mfb + ((ss + 1) & 1) * MF_COLS * XS);
-        __syncthreads();
+      for (int i = 0; i < PER; ++i) {
+        const int ch = min(base + 256 * i, total - 1), c = ch / CPC, j = ch - c * CPC;
+        const int b = a >= 0 ? L.slot[c] / p.k : L.slot[c];
+        v[i] = *reinterpret_cast<const u32x4*>(p.x + (size_t)b * p.H + 8 * j);
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int ch = base + 256 * i, c = ch / CPC, j = ch - c * CPC;
+        if (ch < total) *reinterpret_cast<u32x4*>(mfb + c * XF + 16 * j) = v[i];
+      }
+    }
+    __syncthreads();
+    const bool live = r < nc;
+    const char* xcol = mfb + (live ? r : 0) * XF;
+    for (int s = 0; s < S; s += 2) {
+      mf1_math<FP4, FULL>(p, s, ba, xcol, s * KS * 2, live, ag, au);
+      if (s + 2 < S) mf1_load<FP4, FULL>(p, blob, gl, s + 2, ba, ag[0] + au[0]);
+      if (s + 1 < S) {
+        mf1_math<FP4, FULL>(p, s + 1, bb, xcol, (s + 1) * KS * 2, live, ag, au);
+        if (s + 3 < S) mf1_load<FP4, FULL>(p, blob, gl, s + 3, bb, ag[0] + au[0]);
+      }
+    }
+  } else {
+    {
+      XSeg<KS> x0;
+      x0.load(p, L, a >= 0, 0, nc);
+      x0.store(mfb);
+    }
+    __syncthreads();
+    for (int s = 0; s < S; s += 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ss = s + h;
+        if (ss < S) {
+          XSeg<KS> xn;
+          if (ss + 1 < S) xn.load(p, L, a >= 0, ss + 1, nc);
+          MfBuf& b = h ? bb : ba;
+          mf1_math<FP4, FULL>(p, ss, b, mfb + (ss & 1) * MF_COLS * XS + r * XS, 0, true, ag, au);
+          if (ss + 2 < S) mf1_load<FP4, FULL>(p, blob, gl, ss + 2, b, ag[0] + au[0]);
+          if (ss + 1 < S) xn.store(mfb + ((ss + 1) & 1) * MF_COLS * XS);
+          __syncthreads();
+        }
       }
     }
   }
@@ -1191,11 +1285,14 @@ __device__ __forceinline__ void mf2_load(const LayerParams& p, const uint8_t* do
   }
 }
 
+// hb / lob: this lane's column of the staged h hi / lo halves (column stride
+// applied); hoff: byte offset of segment s inside the column; live: the
+// column exists (else the B fragments are zero).
 template <bool FP4, bool FULL>
-__device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBuf& b, const char* hb, f32x4 (&acc)[2]) {
-  constexpr int KS = FP4 ? 512 : 128, XS = KS * 2 + 16;
-  const char* lob = hb + MF_COLS * XS;  // lo halves follow the hi halves
-  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+__device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBuf& b, const char* hb, const char* lob,
+                                         int hoff, bool live, f32x4 (&acc)[2]) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
+  const u32x4 z{0u, 0u, 0u, 0u};
   if (FP4) {
     const int C2 = p.I / 32;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
@@ -1208,9 +1305,12 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
       for (int t = 0; t < 2; ++t) sc[t] = e8m0_scale(tile_scale<FULL>(b.s[t], kb, q));
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const int off = after(r * XS + (128 * kb + 32 * q + 8 * d) * 2, acc[0][0] + acc[1][0]);
-        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(hb + off);
-        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(lob + off);
+        const bool bv = live && (FULL || c < SC);
+        const int off = after(hoff + (bv ? (128 * kb + 32 * q + 8 * d) * 2 : 0), acc[0][0] + acc[1][0]);
+        const u32x4 rh = *reinterpret_cast<const u32x4*>(hb + off);
+        const u32x4 rl = *reinterpret_cast<const u32x4*>(lob + off);
+        const bf16x8 hi = __builtin_bit_cast(bf16x8, bv ? rh : z);
+        const bf16x8 lo = __builtin_bit_cast(bf16x8, bv ? rl : z);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const bf16x8 wv = fp4x8_bf16(b.q[t][kb][d] & msk, sc[t]);
@@ -1223,10 +1323,11 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool ok = s * 128 + 32 * j + 8 * q < p.Is;
-      const int off = r * XS + (32 * j + 8 * q) * 2;
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(hb + off);
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(lob + off);
-      const u32x4 z{0u, 0u, 0u, 0u};
+      const int off = hoff + (ok ? (32 * j + 8 * q) * 2 : 0);
+      const u32x4 rh = *reinterpret_cast<const u32x4*>(hb + off);
+      const u32x4 rl = *reinterpret_cast<const u32x4*>(lob + off);
+      const bf16x8 hi = __builtin_bit_cast(bf16x8, (live && ok) ? rh : z);
+      const bf16x8 lo = __builtin_bit_cast(bf16x8, (live && ok) ? rl : z);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 wv = __builtin_bit_cast(bf16x8, ok ? b.q[t][j] : z);
@@ -1239,40 +1340,51 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
 
 // h segment [s*KS, s*KS + KS) of the unit's columns (fp32, written by this
 // launch's FC1 units: 8-byte coherent loads) into LDS as bf16 hi and lo.
-template <int KS>
-__device__ __forceinline__ void mf_stage_h(const LayerParams& p, const Lds& L, const float* hsrc, int K, int s, int nc,
-                                           char* hb) {
-  constexpr int XS = KS * 2 + 16, PER = MF_COLS * KS / 2 / 256;  // 8-byte loads per thread
-  uint64_t v[PER];
+// Columns [0, ncols) x elements [k0, k0 + KE) of h (fp32, written by this
+// launch's FC1 units: 8-byte coherent loads, PER per thread per batch) into
+// LDS as bf16 hi halves (column c at hb + c * XS) and lo halves (at
+// hb + lo_off + c * XS).  Elements at or past K, and absent columns, are 0.
+template <int PER>
+__device__ __forceinline__ void mf_stage_h(const LayerParams& p, const Lds& L, const float* hsrc, int K, int k0,
+                                           int KE, int nc, int ncols, char* hb, int XS, int lo_off) {
+  const int HP = KE / 2, total = ncols * HP;  // element pairs
+  for (int base = threadIdx.x; base < total; base += 256 * PER) {
+    uint64_t v[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + 256 * i, c = e / (KS / 2), j = e - c * (KS / 2);
-    const int k0 = s * KS + 2 * j;
-    const bool ok = c < nc && k0 < K;
-    v[i] = ok ? __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(hsrc) + (size_t)L.slot[c] * K + k0),
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-              : 0ull;
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = threadIdx.x + 256 * i, c = e / (KS / 2), j = e - c * (KS / 2);
-    uint32_t hi2 = 0, lo2 = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float f = __uint_as_float((uint32_t)(v[i] >> (32 * h)));
-      const uint16_t hb16 = f32_to_bf16(f);
-      const float rem = f - __uint_as_float((uint32_t)hb16 << 16);
-      hi2 |= (uint32_t)hb16 << (16 * h);
-      lo2 |= (uint32_t)f32_to_bf16(rem) << (16 * h);
+    for (int i = 0; i < PER; ++i) {
+      const int e = base + 256 * i, c = e / HP, j = e - c * HP;
+      const int k = k0 + 2 * j;
+      const bool ok = e < total && c < nc && k < K;
+      v[i] = ok ? __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(hsrc) + (size_t)L.slot[c] * K + k),
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                : 0ull;
     }
-    *reinterpret_cast<uint32_t*>(hb + c * XS + 4 * j) = hi2;
-    *reinterpret_cast<uint32_t*>(hb + MF_COLS * XS + c * XS + 4 * j) = lo2;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = base + 256 * i, c = e / HP, j = e - c * HP;
+      if (e < total) {
+        uint32_t hi2 = 0, lo2 = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float f = __uint_as_float((uint32_t)(v[i] >> (32 * h)));
+          const uint16_t hb16 = f32_to_bf16(f);
+          const float rem = f - __uint_as_float((uint32_t)hb16 << 16);
+          hi2 |= (uint32_t)hb16 << (16 * h);
+          lo2 |= (uint32_t)f32_to_bf16(rem) << (16 * h);
+        }
+        *reinterpret_cast<uint32_t*>(hb + c * XS + 4 * j) = hi2;
+        *reinterpret_cast<uint32_t*>(hb + lo_off + c * XS + 4 * j) = lo2;
+      }
+    }
   }
 }
 
-// FC2 of rows [128 t, 128 t + 128) of H (wave w: row groups 8 t + w and
-// 8 t + w + 4) of routed expert a (FP4) or the shared expert (a < 0), column
-// group cg, once every FC1 tile of that column group is done.
+// FC2 of rows [512 t, 512 t + 512) of H -- four 128-row tiles; in tile mt
+// wave w takes row groups 8 (4 t + mt) + w and + 4 -- of routed expert a
+// (FP4) or the shared expert (a < 0), column group cg, once every FC1 tile of
+// that column group is done.  A narrow column group stages all of h once and
+// runs one pipelined pass per (tile, segment) with no barrier; a wide one
+// stages h per segment.
 template <bool FP4, bool FULL>
 __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
   constexpr int KS = FP4 ? 512 : 128;
@@ -1281,14 +1393,39 @@ __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const int K = FP4 ? p.I : p.Is;
   const int G = p.H / 16;
-  const int gt[2] = {min(8 * t + w, G - 1), min(8 * t + w + 4, G - 1)};
   const uint8_t* down =
       FP4 ? p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * (p.H / 32) * 17 : nullptr;
   const int S = FP4 ? (K / 32 + 15) / 16 : (K + 127) / 128;
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const int MT = min(MF_MT2, (G - 32 * t + 7) / 8);  // 128-row tiles of this unit that exist
+  auto groups = [&](int mt, int (&gt)[2]) {
+    gt[0] = min(8 * (MF_MT2 * t + mt) + w, G - 1);
+    gt[1] = min(8 * (MF_MT2 * t + mt) + w + 4, G - 1);
+  };
+  uint64_t* out = FP4 ? p.or_p : p.os_p;
+  auto emit = [&](int mt, const f32x4 (&acc)[2]) {
+    if (r < nc) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int g = 8 * (MF_MT2 * t + mt) + w + 4 * tt;
+        if (g < G) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            st_pair_f32(out + (size_t)L.slot[r] * p.H + 16 * g + 4 * q + i, acc[tt][i], st.tag);
+        }
+      }
+    }
+  };
+  const int P = MT * S;  // passes: (tile, segment) pairs
   MfBuf ba, bb;
-  mf2_load<FP4, FULL>(p, down, gt, 0, ba, 0.f);  // the weights do not depend on FC1
-  if (S > 1) mf2_load<FP4, FULL>(p, down, gt, 1, bb, 0.f);
+  {  // the weights do not depend on FC1
+    int gt[2];
+    groups(0, gt);
+    mf2_load<FP4, FULL>(p, down, gt, 0, ba, 0.f);
+    if (P > 1) {
+      groups(1 / S, gt);
+      mf2_load<FP4, FULL>(p, down, gt, 1 % S, bb, 0.f);
+    }
+  }
   {  // wait until every FC1 tile of this column group has published its h
     const int ntile = (K + MF_NT1 - 1) / MF_NT1;
     bool ok = true;
@@ -1301,29 +1438,60 @@ __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
     if (!ok) set_error(p);
   }
   const float* hsrc = FP4 ? reinterpret_cast<const float*>(p.hr_p) : reinterpret_cast<const float*>(p.hs_p);
-  for (int s = 0; s < S; s += 2) {
+  const int XF = K * 2 + 16;  // column stride of whole-K staging
+  const bool live = r < nc;
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const f32x4 zero4{0.f, 0.f, 0.f, 0.f};
+  if (2 * nc * XF <= MF_STAGE_BYTES) {
+    __syncthreads();
+    mf_stage_h<16>(p, L, hsrc, K, 0, K, nc, nc, mfb, XF, nc * XF);
+    __syncthreads();
+    const char* hcol = mfb + (live ? r : 0) * XF;
+    for (int pp = 0; pp < P; pp += 2) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ss = s + h;
-      if (ss < S) {
-        __syncthreads();  // the previous segment's h is no longer read
-        mf_stage_h<KS>(p, L, hsrc, K, ss, nc, mfb);
-        __syncthreads();
-        MfBuf& b = h ? bb : ba;
-        mf2_math<FP4, FULL>(p, ss, b, mfb, acc);
-        if (ss + 2 < S) mf2_load<FP4, FULL>(p, down, gt, ss + 2, b, acc[0][0] + acc[1][0]);
+      for (int h = 0; h < 2; ++h) {
+        const int ps = pp + h;
+        if (ps < P) {
+          MfBuf& b = h ? bb : ba;
+          const int mt = ps / S, sg = ps - mt * S;
+          mf2_math<FP4, FULL>(p, sg, b, hcol, hcol + nc * XF, sg * KS * 2, live, acc);
+          if (ps + 2 < P) {
+            int gt[2];
+            groups((ps + 2) / S, gt);
+            mf2_load<FP4, FULL>(p, down, gt, (ps + 2) % S, b, acc[0][0] + acc[1][0]);
+          }
+          if (sg == S - 1) {
+            emit(mt, acc);
+            acc[0] = zero4;
+            acc[1] = zero4;
+          }
+        }
       }
     }
-  }
-  uint64_t* out = FP4 ? p.or_p : p.os_p;
-  if (r < nc) {
+  } else {
+    constexpr int XS = KS * 2 + 16;
+    for (int pp = 0; pp < P; pp += 2) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int g = 8 * t + w + 4 * tt;
-      if (g < G) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st_pair_f32(out + (size_t)L.slot[r] * p.H + 16 * g + 4 * q + i, acc[tt][i], st.tag);
+      for (int h = 0; h < 2; ++h) {
+        const int ps = pp + h;
+        if (ps < P) {
+          const int mt = ps / S, sg = ps - mt * S;
+          __syncthreads();  // the previous segment's h is no longer read
+          mf_stage_h<KS / 32>(p, L, hsrc, K, sg * KS, KS, nc, MF_COLS, mfb, XS, MF_COLS * XS);
+          __syncthreads();
+          MfBuf& b = h ? bb : ba;
+          mf2_math<FP4, FULL>(p, sg, b, mfb + r * XS, mfb + MF_COLS * XS + r * XS, 0, true, acc);
+          if (ps + 2 < P) {
+            int gt[2];
+            groups((ps + 2) / S, gt);
+            mf2_load<FP4, FULL>(p, down, gt, (ps + 2) % S, b, acc[0][0] + acc[1][0]);
+          }
+          if (sg == S - 1) {
+            emit(mt, acc);
+            acc[0] = zero4;
+            acc[1] = zero4;
+          }
+        }
       }
     }
   }
@@ -1363,7 +1531,8 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int rel = u;
     if (rel < p.n_rt) {
-      router_unit<RG>(p, st, L, xs, rel);
+      if constexpr (MF) router_mf_unit(p, st, rel);
+      else router_unit<RG>(p, st, L, xs, rel);
     } else if ((rel -= p.n_rt) < p.n_ro) {
       routing_unit<TPL>(p, st, L, reinterpret_cast<int*>(xs), rel);
     } else if ((rel -= p.n_ro) < p.n_sch) {
@@ -1448,7 +1617,7 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   s.xstride = ((H / 8 + 7) / 8) * 8;
   int K2 = I > Is ? I : Is;
   s.hstride = ((K2 / 4 + 7) / 8) * 8;
-  size_t x_bytes = (size_t)s.rg * s.xstride * 16;
+  size_t x_bytes = B > 1 ? 0 : (size_t)s.rg * s.xstride * 16;  // batch > 1: no x rows in LDS
   // routing reuses this region: top-k survivors and slots, then the
   // schedule's counts (2E) and slot ids (B*k)
   size_t keys_bytes = (size_t)topk_lds_words(E <= 1024 ? 4 : 16) * 4, cnt_bytes = (size_t)(2 * E + B * k) * 4;
@@ -1456,7 +1625,7 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   size_t xr = x_bytes > sched_bytes ? x_bytes : sched_bytes;
   // batch > 1: the MFMA staging buffers (two 16-column segments) alias this
   // region, and no h rows are staged
-  const size_t mf_bytes = (size_t)2 * 16 * (512 * 2 + 16);
+  const size_t mf_bytes = MF_STAGE_BYTES;
   if (B > 1 && mf_bytes > xr) xr = mf_bytes;
   xr = align256(xr);
   s.lds_h_off = (int)xr;
@@ -1521,7 +1690,7 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.n_rt_e = (a.E + 1) / 2;
   p.xstride = sh.xstride;
   p.hstride = sh.hstride;
-  p.n_rb = (a.B + sh.rg - 1) / sh.rg;
+  p.n_rb = a.B > 1 ? (a.B + 15) / 16 : (a.B + sh.rg - 1) / sh.rg;  // batch > 1: 16-row router blocks
   p.n_rt = p.n_rt_e * p.n_rb;
   p.n_ro = a.B;
   p.n_sch = a.B > 1 ? 1 : 0;
