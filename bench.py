@@ -209,15 +209,71 @@ def cpu_baseline(seed=0):
                       "shared + 16 routed experts + combine, single thread; expert regeneration excluded"}
 
 
+def run_stack(stack, steps, warmup, graph=True, seed=0):
+    """Times decode steps of the 8-layer stack (dense block + MoE layer per
+    layer), captured in one HIP graph per step when `graph`."""
+    import numpy as np
+    import torch
+
+    import synth
+    from layer_inputs import h0_host
+    cfg = stack_cfg()
+    h0 = torch.from_numpy(h0_host(cfg, seed)).cuda()
+    h = h0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(1, warmup)):
+            stack.step(h, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            stack.step(h, stream=s)
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    idx = []
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(steps):
+            if g is not None:
+                g.replay()
+            else:
+                stack.step(h, stream=s)
+        e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    idx_h = stack.idx.cpu().numpy()  # routing of the last step
+    H = cfg.hidden
+    nb = synth.expert_bytes(H, cfg.inter)
+    per_layer = [cfg.num_experts * H * 2 + 3 * cfg.shared_inter * H * 2 + int(np.unique(idx_h[l]).size) * nb +
+                 cfg.batch * (H * 2 + 2 * H * 4) + cfg.dense_mats * (H * H * 2 + cfg.batch * 4 * H) +
+                 2 * cfg.batch * (H * 4 + H * 2 + H * 4)
+                 for l in range(cfg.layers)]
+    step_bytes = sum(per_layer)
+    return {"us_per_step": ms * 1e3, "us_per_layer": ms * 1e3 / cfg.layers, "bytes_per_step": step_bytes,
+            "gbps": step_bytes / (ms * 1e-3) / 1e9, "graph": g is not None,
+            "kernels_per_step": cfg.layers * (cfg.dense_mats + 4)}
+
+
+def stack_cfg():
+    from synth import CONFIGS
+    return CONFIGS["k3_stack8"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=6)
-    ap.add_argument("--layers", type=int, default=3, help="distinct layer copies rotated across steps")
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer copies rotated across steps")
     ap.add_argument("--variants", type=int, default=32, help="distinct input rows rotated across steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the batch-8 and batch-64 lines")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 8-layer decode-step stack line")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the scaled HBM traffic of k_moe_layer from two counter CSVs and exit")
     args = ap.parse_args()
@@ -231,25 +287,38 @@ def main():
         sys.exit(2)
 
     import torch
-    from layer_inputs import device_weights
+    from layer_inputs import dense_device, device_weights
     from synth import CONFIGS
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     cfg = CONFIGS["k3_b1"]
-    print(f"[bench] generating {args.layers} K3-shaped layers in HBM", file=sys.stderr, flush=True)
-    layers = [device_weights(cfg, 0, layer=l) for l in range(args.layers)]
+    n_layers = max(args.layers, 0 if args.no_stack else stack_cfg().layers)
+    print(f"[bench] generating {n_layers} K3-shaped layers in HBM", file=sys.stderr, flush=True)
+    layers = [device_weights(cfg, 0, layer=l) for l in range(n_layers)]
     calibration_copy()
     print("[bench] timing batch 1", file=sys.stderr, flush=True)
-    main_r = run_config(cfg, layers, args.steps, args.warmup, args.variants)
+    main_r = run_config(cfg, layers[:args.layers], args.steps, args.warmup, args.variants)
     extra = {}
     if not args.no_extra:
         for name in ("k3_b8", "k3_b64_zipf"):
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-            r = run_config(CONFIGS[name], layers, max(10, args.steps // 2), args.warmup, args.variants)
+            r = run_config(CONFIGS[name], layers[:args.layers], max(10, args.steps // 2), args.warmup, args.variants)
             extra[name] = {"batch": CONFIGS[name].batch, "us_per_layer": round(r["us_per_layer"], 2),
                            "gbps": round(r["gbps"], 1), "frac_peak": round(r["gbps"] / PEAK_GBPS, 4),
                            "distinct_experts": round(r["U_mean"], 1),
                            "kernel_us": {k: round(v, 2) for k, v in r["kernel_us"].items()}}
+    if not args.no_stack:
+        from memory_bound_mxfp4_amd.stack import DecodeStack
+        sc = stack_cfg()
+        print("[bench] timing the 8-layer decode-step stack", file=sys.stderr, flush=True)
+        dense = [dense_device(sc, 0, l) for l in range(sc.layers)]
+        stack = DecodeStack(layers[:sc.layers], dense, sc.batch, sc.rms_eps)
+        r = run_stack(stack, max(5, args.steps // 6), 2)
+        extra["k3_stack8"] = {"batch": sc.batch, "layers": sc.layers, "us_per_step": round(r["us_per_step"], 1),
+                              "us_per_layer": round(r["us_per_layer"], 2), "gbps": round(r["gbps"], 1),
+                              "frac_peak": round(r["gbps"] / PEAK_GBPS, 4), "bytes_per_step": r["bytes_per_step"],
+                              "hip_graph": r["graph"], "kernels_per_step": r["kernels_per_step"]}
+        del stack, dense
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -41,3 +41,20 @@ def k3_layer():
     yield w
     del w
     torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="session")
+def k3_stack():
+    """The 8-layer decode-step stack (seed 0): MoE layers and dense blocks in HBM."""
+    import torch
+    from layer_inputs import dense_device, device_weights
+    from memory_bound_mxfp4_amd.stack import DecodeStack
+    from synth import CONFIGS
+    cfg = CONFIGS["k3_stack8"]
+    print("[fixture] generating the 8-layer stack (seed 0) on the device", flush=True)
+    layers = [device_weights(cfg, 0, layer=l) for l in range(cfg.layers)]
+    dense = [dense_device(cfg, 0, l) for l in range(cfg.layers)]
+    stack = DecodeStack(layers, dense, cfg.batch, cfg.rms_eps)
+    yield stack
+    del stack, layers, dense
+    torch.cuda.empty_cache()
