@@ -14,10 +14,12 @@ routing), so no step finds its weights in cache from an earlier step.
 Bytes are algorithmic: router + shared expert + U distinct experts (counted
 from each step's actual routing) + activations.
 
-Prints ONE JSON line.  `roofline` is for the dominant kernel -- the layer is a
-single persistent kernel, k_moe_layer -- timed with HIP events
-recorded by the library on the launch stream; `cpu_baseline` is the CPU
-oracle on one batch-1 layer (single thread).
+Prints ONE JSON line.  `value` is algorithmic bytes over the wall time of K
+steps launched back to back.  `roofline` is for the dominant kernel -- the
+layer is a single persistent kernel, k_moe_layer -- timed in a second pass
+over the same steps with HIP events recorded by the library around each
+launch on the launch stream; `cpu_baseline` is the CPU oracle on one batch-1
+layer (single thread).
 """
 from __future__ import annotations
 
@@ -77,18 +79,28 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0):
         w.router_bias = bias
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     stream = torch.cuda.current_stream()
+    res_t = [res0[s % variants].clone() for s in range(steps)]  # residuals of the per-kernel-event pass
     try:
         for s in range(warmup):
             w = layers[s % len(layers)]
             moe.moe_decode_layer(w, xs[s % variants], res[s], idx=idx[s], gate=gate[s], ws=ws)
         torch.cuda.synchronize()
+        # Timed pass: K steps launched back to back (the throughput `value`).
         t0 = time.perf_counter()
         for i in range(steps):
             s = warmup + i
             w = layers[s % len(layers)]
-            moe.moe_decode_layer_timed(w, xs[s % variants], res[s], idx[s], gate[s], ws, events[i], stream=stream)
+            moe.moe_decode_layer(w, xs[s % variants], res[s], idx=idx[s], gate=gate[s], ws=ws, stream=stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        # Second pass over the same steps with HIP events recorded by the
+        # library around each kernel on the launch stream (the roofline's
+        # average launch duration).
+        for i in range(steps):
+            s = warmup + i
+            w = layers[s % len(layers)]
+            moe.moe_decode_layer_timed(w, xs[s % variants], res_t[i], idx[s], gate[s], ws, events[i], stream=stream)
+        torch.cuda.synchronize()
     finally:
         for w, b in zip(layers, saved_bias):
             w.router_bias = b
