@@ -88,7 +88,7 @@ struct LayerParams {
   uint64_t* or_p;
   unsigned* ctrl;
   int umax;
-  int n_rt_e;    // router expert pairs (2 experts per unit, 2 waves per expert)
+  int n_rt_e;    // router units per row block (batch 1: 4 experts a unit; else 2)
   int n_rb;      // router row blocks
   int n_rt;      // router units = n_rt_e * n_rb
   int n_ro;      // routing units (one per row)
@@ -118,12 +118,9 @@ __device__ __forceinline__ void set_error(const LayerParams& p) {
 
 struct Lds {  // static LDS of the kernel
   int next;        // next unit index
-  int flag;        // "this workgroup is the last arriver"
-  unsigned tag;    // this call's pair tag
   int U;           // distinct experts (once known)
   int wtot[12];    // scan scratch
   int nrows;       // rows of the current unit
-  double part[4][4];  // router: partial sums of the second half-row waves [wave][row]
   float gates[MOE_MAX_TOPK];  // combine: gates of the current row
   float red[4][4][16][2];     // routed FC1: per-wave partial sums [wave][row][tile row][gate/up]
   int slot[MAX_ROWS];  // slot ids (routed) or batch rows (shared) of the current unit
@@ -429,6 +426,19 @@ __host__ __device__ inline size_t tile_off(int g, int s, int C) {
   return (size_t)g * 16 * C * 17 + (size_t)s * 16 * 272;
 }
 
+// 8 FP4 elements (one dword) -> 8 bf16, exact (E2M1 x 2^k fits bf16), in
+// element order: the A or B operand of one 16x16x32 bf16 MFMA lane.
+__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float s) {
+  bf16x2 t[4];
+  dq4_bf16(w, s, t);
+  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, t[0]), __builtin_bit_cast(uint32_t, t[1]),
+                                          __builtin_bit_cast(uint32_t, t[2]), __builtin_bit_cast(uint32_t, t[3])});
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 struct TileBuf1 {  // one FC1 segment: gate and up codes (4 slabs each) and scale vectors
   u32x4 gq[4], uq[4];
   u32x4 gs, us;
@@ -476,16 +486,23 @@ __device__ __forceinline__ int after(int idx, float dep) {
   return idx;
 }
 
-// FC1 + SwiGLU of one 16-row group g of an expert against RG rows of x (LDS).
-// Wave w takes segments w, w+4, ...; partial sums meet in LDS afterwards.
+// FC1 + SwiGLU of one 16-row group g of an expert against the x row (LDS),
+// on the matrix cores.  Wave w takes segments w, w+4, ...; partial sums meet
+// in LDS afterwards.  Step i = 4 kb + d of a segment is one 16x16x32 MFMA per
+// tile: lane l = 16 q + r supplies row r's elements 8 d .. 8 d + 7 of block
+// 4 kb + q (dword d of its slab kb, decoded to bf16) as the A operand and the
+// matching 8 x values as the B operand, so all 16 columns of the product are
+// the same dot products and lane l ends with rows 4 (l / 16) .. + 3.  This
+// takes the dot products off the vector ALU, which otherwise bounds the
+// stream (the FP4 decode stays there: 4 conversions per dword).
 template <int RG, bool FULL>
 struct Fc1Tile {
+  static_assert(RG == 1, "the batch-1 streams take one row");
   const uint8_t* blob;
   int C1, g, w;
   const u32x4* xs;
   int xstride;
-  int nr;
-  float ag[RG], au[RG];
+  f32x4 ag, au;
   __device__ int seg(int p) const { return w + 4 * p; }
   __device__ void load(TileBuf1& b, int p) {
     const int s = seg(p);
@@ -505,137 +522,109 @@ struct Fc1Tile {
     const int s = seg(p);
     const int q = (threadIdx.x & 63) >> 4;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
-    u32x4 xv[RG];
-#pragma unroll
-    for (int r = 0; r < RG; ++r) xv[r] = (RG == 1 || r < nr) ? xs[r * xstride + xg(s, SC, 0)] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 xv = xs[xg(s, SC, 0)];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kb = i >> 2, d = i & 3;
-      u32x4 xn[RG];
-      if (i < 15) {
-        const int gi = after(after(xg(s, SC, i + 1), ag[0]), au[0]);
-#pragma unroll
-        for (int r = 0; r < RG; ++r) xn[r] = (RG == 1 || r < nr) ? xs[r * xstride + gi] : u32x4{0u, 0u, 0u, 0u};
-      }
+      u32x4 xn;
+      if (i < 15) xn = xs[after(after(xg(s, SC, i + 1), ag[0]), au[0])];
       const int c = 4 * kb + q;
       const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
       const float sg = e8m0_scale(tile_scale<FULL>(b.gs, kb, q));
       const float su = e8m0_scale(tile_scale<FULL>(b.us, kb, q));
-      bf16x2 wg[4], wu[4];
-      dq4_bf16(b.gq[kb][d] & msk, sg, wg);
-      dq4_bf16(b.uq[kb][d] & msk, su, wu);
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        if (RG == 1 || r < nr) {
-          float a0 = ag[r], a1 = au[r];
-          a0 = dot2_bf16(wg[0], xv[r][0], a0);
-          a1 = dot2_bf16(wu[0], xv[r][0], a1);
-          a0 = dot2_bf16(wg[1], xv[r][1], a0);
-          a1 = dot2_bf16(wu[1], xv[r][1], a1);
-          a0 = dot2_bf16(wg[2], xv[r][2], a0);
-          a1 = dot2_bf16(wu[2], xv[r][2], a1);
-          a0 = dot2_bf16(wg[3], xv[r][3], a0);
-          a1 = dot2_bf16(wu[3], xv[r][3], a1);
-          ag[r] = a0;
-          au[r] = a1;
-        }
-      }
-      if (i < 15) {
-#pragma unroll
-        for (int r = 0; r < RG; ++r) xv[r] = xn[r];
-      }
+      const bf16x8 x8 = __builtin_bit_cast(bf16x8, xv);
+      ag = mfma_bf16(fp4x8_bf16(b.gq[kb][d] & msk, sg), x8, ag);
+      au = mfma_bf16(fp4x8_bf16(b.uq[kb][d] & msk, su), x8, au);
+      if (i < 15) xv = xn;
     }
   }
 };
 
-// FC2 of up to two 16-row groups (g0 and g0 + 4) of the down matrix against
-// RG rows of h (fp32, LDS); one pass per segment along I.
+// FC2 of two 16-row groups g0, g0 + 4 (rows of H) of an expert against the h
+// row staged in LDS as bf16 hi and lo parts (h = hi + lo to about 2^-17), on
+// the matrix cores: one 16x16x32 MFMA per tile and step, whose B operand
+// takes hi in the even columns and lo in the odd ones, so that column 0 plus
+// column 1 of the product is the FC2 row against h.  Lane l ends with rows
+// 4 (l / 16) .. + 3 of column l % 16.
 template <int RG, bool FULL>
 struct Fc2Tile {
+  static_assert(RG == 1, "the batch-1 streams take one row");
   const uint8_t* down;  // packed down region of the blob
   int C2, g0, ng;
-  const u32x4* hs;
-  int hstride;
-  int nr;
-  float acc[2][RG];
+  const u32x4* hs;      // hi granules at 0, lo granules at hlo (8 bf16 each, swizzled)
+  int hlo;
+  f32x4 acc[2];
   __device__ void load(TileBuf2& b, int s) {
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       load_tile<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s, C2) + after(after(0, acc[0][0]), acc[1][0]), SC, b.q[t], b.s[t]);
   }
-  // first h granule (4 floats) of step i = 4 kb + d: elements 8 d .. 8 d + 7 of block 4 kb + q
+  // h granule of step i = 4 kb + d (block 4 kb + q of the segment); odd
+  // columns read the lo part
   __device__ int hg(int s, int SC, int i) const {
-    const int q = (threadIdx.x & 63) >> 4, c = 4 * (i >> 2) + q;
-    return (16 * s + (FULL ? c : min(c, SC - 1))) * 8 + 2 * (i & 3);
+    const int l = threadIdx.x & 63, q = l >> 4, c = 4 * (i >> 2) + q;
+    return (l & 1) * hlo + swz((16 * s + (FULL ? c : min(c, SC - 1))) * 4 + (i & 3));
   }
   __device__ void math(const TileBuf2& b, int s) {
     const int q = (threadIdx.x & 63) >> 4;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
-    f32x4 x0[RG], x1[RG];
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const int g = hg(s, SC, 0);
-      x0[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g)]) : f32x4{0, 0, 0, 0};
-      x1[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g + 1)]) : f32x4{0, 0, 0, 0};
-    }
+    u32x4 hv = hs[hg(s, SC, 0)];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kb = i >> 2, d = i & 3;
-      f32x4 n0[RG], n1[RG];
-      if (i < 15) {
-        const int g = after(after(hg(s, SC, i + 1), acc[0][0]), acc[1][0]);
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          n0[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g)]) : f32x4{0, 0, 0, 0};
-          n1[r] = (RG == 1 || r < nr) ? __builtin_bit_cast(f32x4, hs[r * hstride + swz(g + 1)]) : f32x4{0, 0, 0, 0};
-        }
-      }
+      u32x4 hn;
+      if (i < 15) hn = hs[after(after(hg(s, SC, i + 1), acc[0][0]), acc[1][0])];
       const int c = 4 * kb + q;
       const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
-      f32x2 w0[4], w1[4];
-      dq4_f32(b.q[0][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[0], kb, q)), w0);
-      dq4_f32(b.q[1][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[1], kb, q)), w1);
+      const bf16x8 h8 = __builtin_bit_cast(bf16x8, hv);
 #pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        if (RG == 1 || r < nr) {
-          float a = acc[0][r], e = acc[1][r];
-          a = fmaf(w0[0].x, x0[r].x, a);
-          e = fmaf(w1[0].x, x0[r].x, e);
-          a = fmaf(w0[0].y, x0[r].y, a);
-          e = fmaf(w1[0].y, x0[r].y, e);
-          a = fmaf(w0[1].x, x0[r].z, a);
-          e = fmaf(w1[1].x, x0[r].z, e);
-          a = fmaf(w0[1].y, x0[r].w, a);
-          e = fmaf(w1[1].y, x0[r].w, e);
-          a = fmaf(w0[2].x, x1[r].x, a);
-          e = fmaf(w1[2].x, x1[r].x, e);
-          a = fmaf(w0[2].y, x1[r].y, a);
-          e = fmaf(w1[2].y, x1[r].y, e);
-          a = fmaf(w0[3].x, x1[r].z, a);
-          e = fmaf(w1[3].x, x1[r].z, e);
-          a = fmaf(w0[3].y, x1[r].w, a);
-          e = fmaf(w1[3].y, x1[r].w, e);
-          acc[0][r] = a;
-          acc[1][r] = e;
-        }
-      }
-      if (i < 15) {
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          x0[r] = n0[r];
-          x1[r] = n1[r];
-        }
-      }
+      for (int t = 0; t < 2; ++t)
+        acc[t] = mfma_bf16(fp4x8_bf16(b.q[t][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[t], kb, q))), h8, acc[t]);
+      if (i < 15) hv = hn;
     }
   }
 };
 
-// Sum over the four lanes r, r+16, r+32, r+48 that share a tile row.
-__device__ __forceinline__ float sum_q(float v) {
-  v += __shfl_xor(v, 16, WAVE);
-  v += __shfl_xor(v, 32, WAVE);
-  return v;
+// Granule offset of the lo part of an h row staged by stage_h_split: the hi
+// part takes granules [0, K/8) (rounded up to 8), the lo part follows.
+__host__ __device__ inline int h_lo_offset(int K) { return ((K / 8 + 7) / 8) * 8; }
+
+// bf16 round-to-nearest-even of an fp32 value (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The h row of slot L.slot[r] (tagged pairs written earlier in this launch),
+// polled until every pair carries this call's tag, into LDS as two bf16
+// rows: hi = bf16(h) and lo = bf16(h - hi), so that hi + lo is h to within
+// about 2^-17 relative.  Element e sits at bf16 (swz(e / 8), e % 8) of each
+// row (8-element granules, the layout of the x row), lo at granule offset hlo.
+__device__ __forceinline__ void stage_h_split(const LayerParams& p, const WgState& st, u32x4* hs, const uint64_t* src,
+                                              const Lds& L, int r, int K, int hlo) {
+  __syncthreads();
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(hs);
+  const size_t row = (size_t)L.slot[r] * K;
+  bool ok = true;
+  for (int base = threadIdx.x; base < K; base += 256 * 8) {
+    uint64_t v[8];
+    const int n = min(8, (K - base + 255) / 256);
+    ok &= poll_pairs<8>(src, n, [&](int t) { return row + base + 256 * t; }, st.tag, v, SPIN_LIMIT, p.ctrl + CTRL_ERR);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int e = base + 256 * t;
+      if (e < K) {
+        const float h = pair_f32(v[t]);
+        const uint32_t hi = bf16_rne(h);
+        const uint32_t lo = bf16_rne(h - __uint_as_float(hi << 16));
+        h16[swz(e >> 3) * 8 + (e & 7)] = (uint16_t)hi;
+        h16[(hlo + swz(e >> 3)) * 8 + (e & 7)] = (uint16_t)lo;
+      }
+    }
+  }
+  if (!ok) set_error(p);
+  __syncthreads();
 }
 
 // ---- units --------------------------------------------------------------------
@@ -724,30 +713,46 @@ __device__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt
     st_coh(reinterpret_cast<uint64_t*>(p.ctrl + CTRL_READY), make_pair((uint32_t)(wtot[4] + wtot[5] + wtot[6] + wtot[7]), st.tag));
 }
 
-// Router unit: experts 2u and 2u+1 for a block of rows.  Waves 0-1 take the
-// two halves of expert 2u's row, waves 2-3 those of expert 2u+1, so every wave
-// streams 7 KB at H 7168 in one pass of loads; the halves meet in LDS.
-template <int RG>
-__device__ void router_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int u) {
-  const int pe = u % p.n_rt_e, rb = u / p.n_rt_e;
-  const int b0 = rb * RG, nr = min(RG, p.B - b0);
-  load_rows(p, st, L, -1);
-  stage_x(p, st, L, xs, false, b0, nr);
-  const int w = threadIdx.x >> 6, half = w & 1;
-  const int e = 2 * pe + (w >> 1);
-  const int C = p.H / 8, gh = (C + 1) / 2;
-  double acc[RG];
-  router_dot<RG>(p.wr + (size_t)min(e, p.E - 1) * p.H, half * gh, half ? C : gh, xs, p.xstride, nr, acc);
-  if (half && (threadIdx.x & 63) == 0) {
+// Router unit (batch 1): experts 4u .. 4u+3, one per wave; lane l takes
+// 8-element granules l, l + 64, ... of the wave's expert row.  The weight
+// granules and the matching activation granules (read from global memory: the
+// one 14 KB row stays in L2 for every unit) are all requested before any is
+// used, so a unit costs a single memory round trip, and no wave waits for
+// another.  With four experts a unit, the router takes the first quarter of
+// the launch's workgroups -- the first workgroup of each CU, which starts
+// streaming before the CU's second one.  bf16 x bf16 products are exact in
+// fp32 and are summed in fp64.
+__device__ void router_unit(const LayerParams& p, WgState& st, int u) {
+  constexpr int NG = 14;  // granules in flight per lane: a whole row at H 7168
+  const int lane = threadIdx.x & 63;
+  const int e = 4 * u + (threadIdx.x >> 6);
+  const int C = p.H / 8;
+  const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wr + (size_t)min(e, p.E - 1) * p.H);
+  const u32x4* xr = reinterpret_cast<const u32x4*>(p.x);
+  double acc = 0.0;
+  for (int c0 = lane; c0 < C; c0 += 64 * NG) {
+    u32x4 q[NG], xv[NG];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) L.part[w][r] = acc[r];
+    for (int i = 0; i < NG; ++i) {
+      const int c = min(c0 + 64 * i, C - 1);
+      q[i] = ld_weight16(wrow + c);
+      xv[i] = ld16(xr + c);
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const uint32_t msk = (c0 + 64 * i < C) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t wq = q[i][d] & msk;
+        acc += (double)(bf16_lo(wq) * bf16_lo(xv[i][d]));
+        acc += (double)(bf16_hi(wq) * bf16_hi(xv[i][d]));
+      }
+    }
   }
-  __syncthreads();
-  if (!half && e < p.E && (threadIdx.x & 63) == 0) {
+  acc = sum_lanes_f64<64>(acc);
+  if (e < p.E && lane == 0) {
     const double bb = p.bias ? (double)p.bias[e] : 0.0;
-#pragma unroll
-    for (int r = 0; r < RG; ++r)
-      if (r < nr) st_pair_f32(p.logits_p + (size_t)(b0 + r) * p.E + e, (float)(acc[r] + L.part[w + 1][r] + bb), st.tag);
+    st_pair_f32(p.logits_p + e, (float)(acc + bb), st.tag);
   }
 }
 
@@ -812,15 +817,22 @@ __device__ void router_mf_unit(const LayerParams& p, WgState& st, int u) {
 template <int TPL>
 __device__ void routing_unit(const LayerParams& p, WgState& st, Lds& L, int* lds_ints, int b) {
   __builtin_amdgcn_s_setprio(3);  // on the critical path: issue ahead of streaming waves
-  __syncthreads();                // the LDS region is reused
   const size_t s0 = (size_t)b * p.k;
   uint32_t* cand = reinterpret_cast<uint32_t*>(lds_ints);
-  topk_row_wg<TPL>(p.logits_p + (size_t)b * p.E, p.E, p.k, st.tag, SPIN_LIMIT, p.ctrl + CTRL_ERR, cand, p.idx + s0,
-                   p.gate + s0, p.idx_p + s0, p.gate_p + s0, true);
-  __syncthreads();
-  if (!topk_row_wg<TPL>(p.logits_p + (size_t)b * p.E, p.E, p.k, st.tag, SPIN_LIMIT, p.ctrl + CTRL_ERR, cand,
-                        p.idx + s0, p.gate + s0, p.idx_p + s0, p.gate_p + s0, false))
-    set_error(p);
+  // Pass 0 is the dry run, pass 1 the real one.  Both run the SAME instructions
+  // (one copy of the code: the loop is not unrolled and the pass number is
+  // opaque to the compiler), so the dry run leaves exactly the code of the real
+  // pass in the instruction cache.
+#pragma clang loop unroll(disable)
+  for (int pass = 0; pass < 2; ++pass) {
+    int dry = pass == 0;
+    asm volatile("" : "+v"(dry));
+    dry = __builtin_amdgcn_readfirstlane(dry);
+    __syncthreads();  // the LDS region is reused
+    if (!topk_row_wg<TPL>(p.logits_p + (size_t)b * p.E, p.E, p.k, st.tag, SPIN_LIMIT, p.ctrl + CTRL_ERR, cand,
+                          p.idx + s0, p.gate + s0, p.idx_p + s0, p.gate_p + s0, dry != 0))
+      set_error(p);
+  }
   st.x_cached = false;
   __builtin_amdgcn_s_setprio(0);
 }
@@ -874,19 +886,17 @@ __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.w = w;
     f.xs = xs;
     f.xstride = p.xstride;
-    f.nr = nr;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) f.ag[r] = f.au[r] = 0.0f;
+    f.ag = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f.au = f.ag;
     TileBuf1 ba, bb;
     prime_passes(f, P, ba, bb);
     stage_x(p, st, L, xs, true, g0, nr);
     drive_passes(f, P, ba, bb);
+    if ((lane & 15) == 0) {  // column 0: lane 16 q holds rows 4 q .. 4 q + 3
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const float vg = sum_q(f.ag[r]), vu = sum_q(f.au[r]);
-      if (lane < 16) {
-        L.red[w][r][lane][0] = vg;
-        L.red[w][r][lane][1] = vu;
+      for (int i = 0; i < 4; ++i) {
+        L.red[w][0][4 * (lane >> 4) + i][0] = f.ag[i];
+        L.red[w][0][4 * (lane >> 4) + i][1] = f.au[i];
       }
     }
     __syncthreads();
@@ -946,29 +956,29 @@ __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
   const int G = p.H / 16, g0 = 8 * v + w;
   const int ng = g0 < G ? (g0 + 4 < G ? 2 : 1) : 0;
   const int P = ng > 0 ? S2 : 0;
-  for (int r0 = 0; r0 < nrows_unit; r0 += RG) {
-    const int nr = min(RG, nrows_unit - r0);
+  const int hlo = h_lo_offset(p.I);
+  for (int r0 = 0; r0 < nrows_unit; ++r0) {
     Fc2Tile<RG, FULL> f;
     f.down = down;
     f.C2 = C2;
     f.g0 = min(g0, G - 1);
     f.ng = ng;
     f.hs = hs;
-    f.hstride = p.hstride;
-    f.nr = nr;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) f.acc[0][r] = f.acc[1][r] = 0.0f;
+    f.hlo = hlo;
+    f.acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f.acc[1] = f.acc[0];
     TileBuf2 ba, bb;
     prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
-    stage_h(p, st, hs, p.hr_p, L, r0, nr, p.I);
+    stage_h_split(p, st, hs, p.hr_p, L, r0, p.I, hlo);
     drive_passes(f, P, ba, bb);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const float val = sum_q(f.acc[t][r]);
-        if ((RG == 1 || r < nr) && lane < 16 && t < ng)
-          st_pair_f32(p.or_p + (size_t)L.slot[r0 + r] * p.H + 16 * (g0 + 4 * t) + lane, val, st.tag);
+      for (int i = 0; i < 4; ++i) {
+        // column 0 (hi part) plus column 1 (lo part): lanes 16 q and 16 q + 1
+        const float val = f.acc[t][i] + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(f.acc[t][i])));
+        if ((lane & 15) == 0 && t < ng)
+          st_pair_f32(p.or_p + (size_t)L.slot[r0] * p.H + 16 * (g0 + 4 * t) + 4 * (lane >> 4) + i, val, st.tag);
       }
     }
   }
@@ -1037,17 +1047,6 @@ constexpr int MF_NT2 = 128 * MF_MT2;  // FC2 rows of H per unit
 constexpr int MF_XS_FP4 = 512 * 2 + 16;  // LDS column stride (bytes) of a 512-element segment
 constexpr int MF_XS_BF = 128 * 2 + 16;   // ... of a 128-element segment (bf16 weights)
 constexpr int MF_STAGE_BYTES = 2 * MF_COLS * MF_XS_FP4;  // LDS staging region of the MFMA units
-
-__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float s) {
-  bf16x2 t[4];
-  dq4_bf16(w, s, t);
-  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, t[0]), __builtin_bit_cast(uint32_t, t[1]),
-                                          __builtin_bit_cast(uint32_t, t[2]), __builtin_bit_cast(uint32_t, t[3])});
-}
-
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // Column list of a unit: batch rows 16 cg .. of the shared expert (a < 0),
 // or rows 16 cg .. of active expert a's row list (slot ids).
@@ -1511,12 +1510,12 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   char* mfb = reinterpret_cast<char*>(lds_raw);  // MFMA staging (aliases the x region: one unit at a time)
   int* sched_lds = reinterpret_cast<int*>(reinterpret_cast<char*>(lds_raw) + p.lds_sched_off);
   __shared__ Lds L;
-  if (threadIdx.x == 0) {
-    const uint32_t epoch = ld_coh(p.ctrl + CTRL_EPOCH);
-    L.tag = (epoch == 0xFFFFFFFFu) ? 1u : epoch + 1u;  // never 0: a cleared workspace holds no valid pair
-  }
-  __syncthreads();
-  WgState st{false, false, 0, L.tag, nullptr, nullptr, nullptr, nullptr};
+  // Every thread loads the call epoch itself: the value is only needed by the
+  // first hand-over, so the load overlaps the first unit's weight loads
+  // instead of costing a round trip (and a barrier) before any of them.
+  const uint32_t epoch = ld_coh(p.ctrl + CTRL_EPOCH);
+  const uint32_t tag = (epoch == 0xFFFFFFFFu) ? 1u : epoch + 1u;  // never 0: a cleared workspace holds no valid pair
+  WgState st{false, false, 0, tag, nullptr, nullptr, nullptr, nullptr};
   // The first units (router, routing, shared FC1) go by workgroup index, so
   // the launch ramp does not queue on the head counter.
   int u = (int)blockIdx.x < p.n_static ? (int)blockIdx.x : -1;
@@ -1532,7 +1531,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     int rel = u;
     if (rel < p.n_rt) {
       if constexpr (MF) router_mf_unit(p, st, rel);
-      else router_unit<RG>(p, st, L, xs, rel);
+      else router_unit(p, st, rel);
     } else if ((rel -= p.n_rt) < p.n_ro) {
       routing_unit<TPL>(p, st, L, reinterpret_cast<int*>(xs), rel);
     } else if ((rel -= p.n_ro) < p.n_sch) {
@@ -1591,7 +1590,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     if (old == gridDim.x - 1) {
       st_coh(p.ctrl + CTRL_HEAD, 0u);
       st_coh(p.ctrl + CTRL_EXIT, 0u);
-      st_coh(p.ctrl + CTRL_EPOCH, L.tag);  // the next call's tag is L.tag + 1
+      st_coh(p.ctrl + CTRL_EPOCH, st.tag);  // the next call's tag is L.tag + 1
     }
   }
 }
@@ -1616,7 +1615,8 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   if (B > 1) s.full = (H % 512 == 0) && (I % 512 == 0);  // the MFMA path: every packed tile is complete
   s.xstride = ((H / 8 + 7) / 8) * 8;
   int K2 = I > Is ? I : Is;
-  s.hstride = ((K2 / 4 + 7) / 8) * 8;
+  s.hstride = ((K2 / 4 + 7) / 8) * 8;  // fp32 h rows (shared expert FC2)
+  if (B == 1 && 2 * h_lo_offset(I) > s.hstride) s.hstride = 2 * h_lo_offset(I);  // bf16 hi + lo rows (routed FC2)
   size_t x_bytes = B > 1 ? 0 : (size_t)s.rg * s.xstride * 16;  // batch > 1: no x rows in LDS
   // routing reuses this region: top-k survivors and slots, then the
   // schedule's counts (2E) and slot ids (B*k)
@@ -1687,7 +1687,7 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.ctrl = a.ws.ctrl;
   p.umax = a.ws.umax;
   const LaunchShape sh = launch_shape(a.H, a.I, a.E, a.k, a.Is, a.B);
-  p.n_rt_e = (a.E + 1) / 2;
+  p.n_rt_e = a.B > 1 ? (a.E + 1) / 2 : (a.E + 3) / 4;  // batch 1: 4 experts a unit, else 2
   p.xstride = sh.xstride;
   p.hstride = sh.hstride;
   p.n_rb = a.B > 1 ? (a.B + 15) / 16 : (a.B + sh.rg - 1) / sh.rg;  // batch > 1: 16-row router blocks

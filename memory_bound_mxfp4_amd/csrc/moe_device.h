@@ -128,31 +128,59 @@ __device__ __forceinline__ bool poll_pairs(const uint64_t* p, int n, Idx idx, ui
 // ---------------------------------------------------------------------------
 // Workgroup top-k of one row (4 waves), for the fused layer kernel.  Order:
 // (key desc, index asc) on order-preserving integer keys, so ties go to the
-// lower expert index.  No serial k-round tournament: every step is a short
-// loop of independent compares.
+// lower expert index; an entry is packed as key << 32 | ~index, so that order
+// is plain 64-bit unsigned order (0 = no entry).  Every step is a short run
+// of independent operations -- no serial rounds over the experts:
 //   1. wave w holds experts [w Q, (w+1) Q), Q = ceil(E/4), <= TPL per lane;
 //      each lane takes the best of its own entries;
-//   2. the wave ranks its 64 lane-bests (each against all 64) and takes T_w
-//      = the k-th best of them.  At most k-1 entries of the wave beat T_w, so
-//      T_w is no better than the wave's k-th best entry, which in turn is no
-//      better than the row's k-th best.  Hence T = the best of the four T_w
-//      is also no better than the row's k-th best: keeping only entries at
-//      least as good as T loses none of the row's top k (at most
-//      4 ((k-1) TPL + 1) entries survive; typically a few more than k);
+//   2. the lanes are cut into G = (k rounded up to a power of two) groups of
+//      64/G consecutive lanes, each group spanning all four waves; its best
+//      entry comes from a few DPP steps per wave and a max over the waves.
+//      T = the worst of the G group bests: the G groups are disjoint, so at
+//      least G >= k entries are at least as good as T, i.e. T is no better
+//      than the row's k-th best, and keeping the entries at least as good as
+//      T loses none of the top k (about 50 survive at E 896, k 16);
 //   3. survivors are compacted into LDS (ballot + prefix count + one LDS
 //      atomic per wave);
-//   4. every survivor is ranked against all survivors; rank j < k is slot j.
-// LDS `cand`: topk_lds_words(TPL) 32-bit words.
+//   4. every survivor is ranked against all survivors, the comparisons split
+//      over 1, 2 or 4 adjacent lanes whose counts are added by DPP; rank
+//      j < k is slot j.
+// LDS `cand`: topk_lds_words(TPL) 32-bit words, 16-byte aligned.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool beats(uint32_t ka, uint32_t ia, uint32_t kb, uint32_t ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-__host__ __device__ constexpr int topk_lds_words(int tpl) { return 4 * 64 * tpl * 2 + 8 + 1 + 2 * 64; }
+__host__ __device__ constexpr int topk_lds_words(int tpl) { return 4 * 64 * 2 + 4 * 64 * tpl * 2 + 4 + 2 * 64; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m), hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Max (MAX) or min over each block of `bs` consecutive lanes (bs a power of
+// two, wave-uniform); every lane of a block ends with its block's result.
+template <bool MAX>
+__device__ __forceinline__ uint64_t block_reduce_u64(uint64_t v, int bs) {
+  auto op = [](uint64_t a, uint64_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  if (bs >= 2) v = op(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+  if (bs >= 4) v = op(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+  if (bs >= 8) v = op(v, dpp_u64<0x141>(v));  // row_half_mirror
+  if (bs >= 16) v = op(v, dpp_u64<0x140>(v)); // row_mirror
+  if (bs >= 32) v = op(v, shfl_xor_u64(v, 16));
+  if (bs >= 64) v = op(v, shfl_xor_u64(v, 32));
+  return v;
+}
 
 // dry: one pass over whatever the logits hold, no outputs -- run while the
 // router is still working, it brings this code into the instruction cache so
-// the real pass does not stall on cold instruction fetches.
+// the real pass does not wait on instruction fetches.
 template <int TPL>
 __device__ __forceinline__ bool topk_row_wg(const uint64_t* __restrict__ l, int E, int k, uint32_t tag,
                                             unsigned limit, const unsigned* err, uint32_t* cand,
@@ -160,63 +188,52 @@ __device__ __forceinline__ bool topk_row_wg(const uint64_t* __restrict__ l, int 
                                             uint64_t* idx_p, uint64_t* gate_p, bool dry) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int Q = (E + 3) / 4, e0 = w * Q, e1 = min(E, e0 + Q);
-  uint32_t* surv = cand;                      // [4 * 64 TPL] (key, index) pairs
-  uint32_t* thr = cand + 4 * 64 * TPL * 2;    // [4] (key, index) threshold of each wave
-  uint32_t* nsurv = thr + 8;                  // survivor count
-  uint32_t* out = nsurv + 1;                  // [64] (key, index) of slots 0..63
+  int G = 1;
+  while (G < k) G <<= 1;
+  const int bs = 64 / G;
+  uint64_t* gbest = reinterpret_cast<uint64_t*>(cand);  // [4 waves][64] group bests
+  uint32_t* surv = cand + 4 * 64 * 2;                    // [4 * 64 TPL] (key, index) pairs
+  uint32_t* nsurv = surv + 4 * 64 * TPL * 2;             // survivor count
+  uint32_t* out = nsurv + 4;                             // [64] (key, index) of slots 0..63
   if (threadIdx.x == 0) *nsurv = 0u;
   bool ok;
   uint32_t key[TPL], ix[TPL];
+  uint64_t pk[TPL];
   {
     uint64_t lv[TPL];
     const int mine = max(0, min(TPL, (e1 - e0 - lane + 63) / 64));
     ok = poll_pairs<TPL>(l, max(mine, 1), [&](int i) { return min(e0 + lane + 64 * i, E - 1); }, tag, lv,
                          dry ? 0u : limit, err) || dry;
-    uint32_t bk = 0u, bi = 0xFFFFFFFFu;  // this lane's best (key 0 = no entry)
+    uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       const int e = e0 + lane + 64 * i;
       key[i] = e < e1 ? order_key(pair_f32(lv[i])) : 0u;
-      ix[i] = e < e1 ? (uint32_t)e : 0xFFFFFFFFu;
-      if (key[i] != 0u && beats(key[i], ix[i], bk, bi)) {
-        bk = key[i];
-        bi = ix[i];
-      }
+      ix[i] = (uint32_t)e;
+      pk[i] = key[i] != 0u ? ((uint64_t)key[i] << 32) | (0xFFFFFFFFu - ix[i]) : 0ull;
+      best = pk[i] > best ? pk[i] : best;
     }
-    // rank of this lane's best among the wave's 64 lane-bests
-    int r = 0;
-#pragma unroll 16
-    for (int j = 0; j < 64; ++j) {
-      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)bk, j);
-      const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)bi, j);
-      r += beats(kj, ij, bk, bi) ? 1 : 0;
-    }
-    const uint64_t th = __ballot(bk != 0u && r == k - 1);
-    uint32_t tk = 0u, ti = 0xFFFFFFFFu;  // no threshold: fewer than k lanes hold entries
-    if (th != 0ull) {
-      const int tl = __ffsll((long long)th) - 1;
-      tk = (uint32_t)__builtin_amdgcn_readlane((int)bk, tl);
-      ti = (uint32_t)__builtin_amdgcn_readlane((int)bi, tl);
-    }
-    if (lane == 0) {
-      thr[2 * w] = tk;
-      thr[2 * w + 1] = ti;
-    }
+    best = block_reduce_u64<true>(best, bs);
+    if ((lane & (bs - 1)) == 0) gbest[w * 64 + lane / bs] = best;
   }
   __syncthreads();
-  uint32_t tk = thr[0], ti = thr[1];
-#pragma unroll
-  for (int v = 1; v < 4; ++v)
-    if (beats(thr[2 * v], thr[2 * v + 1], tk, ti)) {
-      tk = thr[2 * v];
-      ti = thr[2 * v + 1];
+  uint64_t T;
+  {
+    uint64_t g = ~0ull;  // neutral for the min
+    if (lane < G) {
+      const uint64_t a = max(gbest[lane], gbest[64 + lane]), b = max(gbest[128 + lane], gbest[192 + lane]);
+      g = max(a, b);
     }
+    g = block_reduce_u64<false>(g, G);
+    T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(g >> 32), 0) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)g, 0);
+  }
   {
     bool keep[TPL];
     uint32_t n = 0;
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
-      keep[i] = key[i] != 0u && !beats(tk, ti, key[i], ix[i]);
+      keep[i] = pk[i] != 0ull && pk[i] >= T;
       n += (uint32_t)__popcll(__ballot(keep[i]));
     }
     uint32_t base = 0;
@@ -234,20 +251,33 @@ __device__ __forceinline__ bool topk_row_wg(const uint64_t* __restrict__ l, int 
     }
   }
   __syncthreads();
-  // rank every survivor against all survivors (broadcast LDS reads, 4 per batch)
+  // rank every survivor against all survivors; survivor s is compared by the
+  // `parts` adjacent threads s * parts + (0 .. parts-1), each taking an even
+  // stretch of the list (two entries per 16-byte LDS read)
   const uint32_t n = *nsurv;
-  for (uint32_t t = threadIdx.x; t < n; t += 256) {
-    const uint32_t mk = surv[2 * t], mi = surv[2 * t + 1];
+  const int lp = n <= 64u ? 2 : (n <= 128u ? 1 : 0);  // log2(parts)
+  const uint32_t span = (((n + (1u << lp) - 1) >> lp) + 1u) & ~1u;
+  for (uint32_t base = 0; base < (n << lp); base += 256) {
+    const uint32_t t = base + threadIdx.x, sidx = t >> lp, part = t & ((1u << lp) - 1u);
+    const bool live = sidx < n;
+    uint32_t mk = 0, mi = 0;
     int r = 0;
-    uint32_t j = 0;
-    for (; j + 4 <= n; j += 4) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(surv + 2 * j);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(surv + 2 * j + 4);
-      r += (beats(a[0], a[1], mk, mi) ? 1 : 0) + (beats(a[2], a[3], mk, mi) ? 1 : 0) +
-           (beats(b[0], b[1], mk, mi) ? 1 : 0) + (beats(b[2], b[3], mk, mi) ? 1 : 0);
+    if (live) {
+      mk = surv[2 * sidx];
+      mi = surv[2 * sidx + 1];
+      const uint32_t j0 = min(n, part * span), j1 = min(n, j0 + span);
+      uint32_t j = j0;
+      for (; j + 4 <= j1; j += 4) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(surv + 2 * j);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(surv + 2 * j + 4);
+        r += (beats(a[0], a[1], mk, mi) ? 1 : 0) + (beats(a[2], a[3], mk, mi) ? 1 : 0) +
+             (beats(b[0], b[1], mk, mi) ? 1 : 0) + (beats(b[2], b[3], mk, mi) ? 1 : 0);
+      }
+      for (; j < j1; ++j) r += beats(surv[2 * j], surv[2 * j + 1], mk, mi) ? 1 : 0;
     }
-    for (; j < n; ++j) r += beats(surv[2 * j], surv[2 * j + 1], mk, mi) ? 1 : 0;
-    if (r < k) {
+    if (lp >= 1) r += (int)dpp_u32<0xB1>((uint32_t)r);  // quad_perm [1,0,3,2]: the partner lane's count
+    if (lp >= 2) r += (int)dpp_u32<0x4E>((uint32_t)r);  // quad_perm [2,3,0,1]
+    if (live && part == 0u && r < k) {
       out[2 * r] = mk;
       out[2 * r + 1] = mi;
     }
