@@ -476,6 +476,44 @@ __device__ __forceinline__ void load_tile(const uint8_t* t, int SC, u32x4 (&cq)[
   }
 }
 
+// One 1 KB slab kb of a tile's codes (lane 16 q + r: block 4 kb + q of row
+// r), and the tile's scale vector, as load_tile reads them.
+template <bool FULL>
+__device__ __forceinline__ u32x4 load_slab(const uint8_t* t, int SC, int kb) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  if (FULL) return ld_weight16(t + kb * 1024 + l * 16);
+  return ld_weight16(t + min(4 * kb + q, SC - 1) * 256 + r * 16);
+}
+
+template <bool FULL>
+__device__ __forceinline__ u32x4 load_scales(const uint8_t* t, int SC) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  if (FULL) return ld_weight16(t + 4096 + r * 16);
+  uint32_t b = 0;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) b |= (uint32_t)t[SC * 256 + r * SC + min(4 * kb + q, SC - 1)] << (8 * kb);
+  return u32x4{b, 0u, 0u, 0u};
+}
+
+// An address offset (always 0) that the compiler must compute after `dep`:
+// it ties a refill load to the last use of the registers it overwrites, so the
+// load is neither hoisted into fresh registers nor delayed.
+__device__ __forceinline__ int after_u(int idx, uint32_t dep) {
+  asm volatile("" : "+v"(idx) : "v"(dep));
+  return idx;
+}
+
+// Drives P passes of a tile stream whose math refills the buffer it has just
+// consumed with the pass after next, slab by slab (math(buf, p, refill)).
+// Two passes stay in flight all the time, also while a pass's math runs.
+template <class Buf, class Traits>
+__device__ __forceinline__ void drive_rolling(Traits& t, int P, Buf& a, Buf& b) {
+  for (int p = 0; p < P; p += 2) {
+    t.math(a, p, p + 2 < P);
+    if (p + 1 < P) t.math(b, p + 1, p + 3 < P);
+  }
+}
+
 // The LDS reads of a pass's activations are software-pipelined one step
 // ahead of the math, and each read's address is tied (through an empty asm)
 // to the accumulator of the step before, so the compiler cannot hoist every
@@ -518,24 +556,52 @@ struct Fc1Tile {
     const int q = (threadIdx.x & 63) >> 4, c = 4 * (i >> 2) + q;
     return swz((16 * s + (FULL ? c : min(c, SC - 1))) * 4 + (i & 3));
   }
-  __device__ void math(const TileBuf1& b, int p) {
+  // The x granules are read one slab ahead; slab kb of both tiles is
+  // refilled with pass p + 2 as soon as its last dword is decoded, the scale
+  // vectors after the last slab.
+  __device__ void math(TileBuf1& b, int p, bool refill) {
     const int s = seg(p);
     const int q = (threadIdx.x & 63) >> 4;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
-    u32x4 xv = xs[xg(s, SC, 0)];
+    const int s2 = seg(p + 2);
+    const int SC2 = FULL ? 16 : min(16, C1 - 16 * s2);
+    const uint8_t* gt2 = blob + 2 * tile_off(g, refill ? s2 : s, C1);
+    u32x4 xv[4], xn[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kb = i >> 2, d = i & 3;
-      u32x4 xn;
-      if (i < 15) xn = xs[after(after(xg(s, SC, i + 1), ag[0]), au[0])];
+    for (int d = 0; d < 4; ++d) xv[d] = xs[xg(s, SC, d)];
+    int o = 0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < 3) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xn[d] = xs[after(xg(s, SC, 4 * kb + 4 + d), ag[0])];
+      }
       const int c = 4 * kb + q;
       const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
       const float sg = e8m0_scale(tile_scale<FULL>(b.gs, kb, q));
       const float su = e8m0_scale(tile_scale<FULL>(b.us, kb, q));
-      const bf16x8 x8 = __builtin_bit_cast(bf16x8, xv);
-      ag = mfma_bf16(fp4x8_bf16(b.gq[kb][d] & msk, sg), x8, ag);
-      au = mfma_bf16(fp4x8_bf16(b.uq[kb][d] & msk, su), x8, au);
-      if (i < 15) xv = xn;
+      bf16x8 wg, wu;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        wg = fp4x8_bf16(b.gq[kb][d] & msk, sg);
+        wu = fp4x8_bf16(b.uq[kb][d] & msk, su);
+        const bf16x8 x8 = __builtin_bit_cast(bf16x8, xv[d]);
+        ag = mfma_bf16(wg, x8, ag);
+        au = mfma_bf16(wu, x8, au);
+      }
+      if (refill) {
+        o = after_u(after_u(o, __builtin_bit_cast(u32x4, wg)[3]), __builtin_bit_cast(u32x4, wu)[3]);
+        b.gq[kb] = load_slab<FULL>(gt2 + o, SC2, kb);
+        b.uq[kb] = load_slab<FULL>(gt2 + SC2 * 272 + o, SC2, kb);
+      }
+      if (kb < 3) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xv[d] = xn[d];
+      }
+    }
+    if (refill) {
+      b.gs = load_scales<FULL>(gt2 + o, SC2);
+      b.us = load_scales<FULL>(gt2 + SC2 * 272 + o, SC2);
     }
   }
 };
@@ -566,22 +632,45 @@ struct Fc2Tile {
     const int l = threadIdx.x & 63, q = l >> 4, c = 4 * (i >> 2) + q;
     return (l & 1) * hlo + swz((16 * s + (FULL ? c : min(c, SC - 1))) * 4 + (i & 3));
   }
-  __device__ void math(const TileBuf2& b, int s) {
+  __device__ void math(TileBuf2& b, int s, bool refill) {
     const int q = (threadIdx.x & 63) >> 4;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
-    u32x4 hv = hs[hg(s, SC, 0)];
+    const int SC2 = FULL ? 16 : min(16, C2 - 16 * (s + 2));
+    u32x4 hv[4], hn[4];  // h granules of this slab and of the next (read one slab ahead)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kb = i >> 2, d = i & 3;
-      u32x4 hn;
-      if (i < 15) hn = hs[after(after(hg(s, SC, i + 1), acc[0][0]), acc[1][0])];
+    for (int d = 0; d < 4; ++d) hv[d] = hs[hg(s, SC, d)];
+    int o = 0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < 3) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) hn[d] = hs[after(hg(s, SC, 4 * kb + 4 + d), acc[0][0])];
+      }
       const int c = 4 * kb + q;
       const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
-      const bf16x8 h8 = __builtin_bit_cast(bf16x8, hv);
+      bf16x8 wv[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        acc[t] = mfma_bf16(fp4x8_bf16(b.q[t][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[t], kb, q))), h8, acc[t]);
-      if (i < 15) hv = hn;
+      for (int d = 0; d < 4; ++d) {
+        const bf16x8 h8 = __builtin_bit_cast(bf16x8, hv[d]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          wv[t] = fp4x8_bf16(b.q[t][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[t], kb, q)));
+          acc[t] = mfma_bf16(wv[t], h8, acc[t]);
+        }
+      }
+      if (refill) {
+        o = after_u(after_u(o, __builtin_bit_cast(u32x4, wv[0])[3]), __builtin_bit_cast(u32x4, wv[1])[3]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) b.q[t][kb] = load_slab<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s + 2, C2) + o, SC2, kb);
+      }
+      if (kb < 3) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) hv[d] = hn[d];
+      }
+    }
+    if (refill) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) b.s[t] = load_scales<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s + 2, C2) + o, SC2);
     }
   }
 };
@@ -891,7 +980,7 @@ __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     TileBuf1 ba, bb;
     prime_passes(f, P, ba, bb);
     stage_x(p, st, L, xs, true, g0, nr);
-    drive_passes(f, P, ba, bb);
+    drive_rolling(f, P, ba, bb);
     if ((lane & 15) == 0) {  // column 0: lane 16 q holds rows 4 q .. 4 q + 3
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -970,7 +1059,7 @@ __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     TileBuf2 ba, bb;
     prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
     stage_h_split(p, st, hs, p.hr_p, L, r0, p.I, hlo);
-    drive_passes(f, P, ba, bb);
+    drive_rolling(f, P, ba, bb);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
