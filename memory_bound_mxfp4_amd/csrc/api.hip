@@ -47,7 +47,7 @@ Workspace ws_layout(void* base, int H, int I, int E, int k, int Is, int B) {
   w.or_p = reinterpret_cast<uint64_t*>(take(8 * slots * H));
   w.sched.cg_off = reinterpret_cast<int*>(take(sizeof(int) * (umax + 1)));
   const int n1 = I > Is ? I : Is;
-  w.hflag_tiles = (n1 + 63) / 64;
+  w.hflag_tiles = (n1 + 15) / 16;  // routed FC1 flags per 64-row tile, shared ones per 16-row group
   w.hflag = reinterpret_cast<uint64_t*>(take(8 * (umax + 1) * 4 * (size_t)w.hflag_tiles));
   w.bytes = o;
   return w;

@@ -99,8 +99,9 @@ struct LayerParams {
   int n_r2;      // routed FC2 units per expert
   int n_tile;    // combine tiles over H
   int mf_t1;     // batch > 1: routed FC1 units per column group (64 rows of I each)
-  int mf_t1s;    // batch > 1: shared FC1 units per column group (64 rows of Is each)
-  int mf_t2;     // batch > 1: FC2 units per column group (128 rows of H each)
+  int mf_t1s;    // batch > 1: shared FC1 units per column group (16 rows of Is each)
+  int mf_t2;     // batch > 1: routed FC2 units per column group (MF_NT2 rows of H each)
+  int mf_t2s;    // batch > 1: shared FC2 units per column group (128 rows of H each)
   int mf_cgs;    // batch > 1: shared-expert column groups (16 batch rows each)
   int n_front;   // units before the routed ones (router .. shared FC1)
   int n_static;  // units 0 .. n_static-1 go to workgroups 0 .. n_static-1
@@ -1348,6 +1349,77 @@ __device__ void mf_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
   if (threadIdx.x == 0) st_coh(hflag_at(p, a < 0 ? p.umax : a, cg, t), make_pair(1u, st.tag));
 }
 
+// Shared-expert FC1 + SwiGLU at batch > 1 (bf16 weights): one 16-row group g
+// of Is for column group cg.  The four waves split K -- wave w takes the
+// 128-element segments w, w + 4, ... -- so a unit is one row group's 458 KB
+// (at K3's shape) like a routed unit, not four; the B operand (8 x values of
+// the lane's column and k-slot) is read straight from global memory, where
+// the B rows of x stay in L2, so no staging or barrier interrupts the
+// stream.  Partial sums meet in LDS; h goes out as fp32 with coherent stores,
+// then the group's "done" flag (after every store has completed).
+template <bool FULL>
+__device__ void mf_sh1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int cg, int g) {
+  load_cols(p, st, L, -1, cg);
+  const int nc = L.nrows;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int S = (p.H + 127) / 128;
+  const int P = w < S ? (S - w + 3) / 4 : 0;
+  const bool live = r < nc;
+  const uint16_t* xrow = p.x + (size_t)L.slot[live ? r : 0] * p.H;
+  const u32x4 z{0u, 0u, 0u, 0u};
+  f32x4 ag{0.f, 0.f, 0.f, 0.f}, au{0.f, 0.f, 0.f, 0.f};
+  MfBuf ba, bb;
+  u32x4 xa[4], xb[4];
+  auto load = [&](MfBuf& b, u32x4 (&xv)[4], int pp, float dep) {
+    const int s = w + 4 * pp;
+    mf1_load<false, FULL>(p, nullptr, g, s, b, dep);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = ld16(xrow + min(s * 128 + 32 * j + 8 * q, p.H - 8) + after(0, dep));
+  };
+  auto math = [&](const MfBuf& b, const u32x4 (&xv)[4], int pp) {
+    const int s = w + 4 * pp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = s * 128 + 32 * j + 8 * q < p.H;
+      const bf16x8 x8 = __builtin_bit_cast(bf16x8, (live && ok) ? xv[j] : z);
+      ag = mfma_bf16(__builtin_bit_cast(bf16x8, ok ? b.q[0][j] : z), x8, ag);
+      au = mfma_bf16(__builtin_bit_cast(bf16x8, ok ? b.q[1][j] : z), x8, au);
+    }
+  };
+  if (P > 0) load(ba, xa, 0, 0.f);
+  if (P > 1) load(bb, xb, 1, 0.f);
+  for (int pp = 0; pp < P; pp += 2) {
+    math(ba, xa, pp);
+    if (pp + 2 < P) load(ba, xa, pp + 2, ag[0] + au[0]);
+    if (pp + 1 < P) {
+      math(bb, xb, pp + 1);
+      if (pp + 3 < P) load(bb, xb, pp + 3, ag[0] + au[0]);
+    }
+  }
+  // waves' partial sums: lane (q, r) holds rows 4 q + i of column r
+  float* red = reinterpret_cast<float*>(mfb);  // [4 waves][2][16 rows][16 columns]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[((w * 2 + 0) * 16 + 4 * q + i) * 16 + r] = ag[i];
+    red[((w * 2 + 1) * 16 + 4 * q + i) * 16 + r] = au[i];
+  }
+  __syncthreads();
+  {
+    const int row = threadIdx.x >> 4, col = threadIdx.x & 15, n = 16 * g + row;
+    float vg = 0.f, vu = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      vg += red[((ww * 2 + 0) * 16 + row) * 16 + col];
+      vu += red[((ww * 2 + 1) * 16 + row) * 16 + col];
+    }
+    if (col < nc && n < p.Is)
+      st_coh(reinterpret_cast<uint32_t*>(p.hs_p) + (size_t)L.slot[col] * p.Is + n, __float_as_uint(silu_f(vg) * vu));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every thread's h stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) st_coh(hflag_at(p, p.umax, cg, g), make_pair(1u, st.tag));
+}
+
 // One FC2 segment of a wave: two 16-row A tiles of the down matrix.
 //   FP4:  q[t][kb] = packed slab kb of tile t, s[t] its scales
 //   bf16: q[t][j]  = 8 elements of row r of tile t at s*128 + 32 j + 8 q
@@ -1484,17 +1556,18 @@ __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
   const uint8_t* down =
       FP4 ? p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * (p.H / 32) * 17 : nullptr;
   const int S = FP4 ? (K / 32 + 15) / 16 : (K + 127) / 128;
-  const int MT = min(MF_MT2, (G - 32 * t + 7) / 8);  // 128-row tiles of this unit that exist
+  constexpr int MT2 = FP4 ? MF_MT2 : 1;  // 128-row tiles per unit (shared expert: one, 393 KB of bf16)
+  const int MT = min(MT2, (G - 8 * MT2 * t + 7) / 8);  // 128-row tiles of this unit that exist
   auto groups = [&](int mt, int (&gt)[2]) {
-    gt[0] = min(8 * (MF_MT2 * t + mt) + w, G - 1);
-    gt[1] = min(8 * (MF_MT2 * t + mt) + w + 4, G - 1);
+    gt[0] = min(8 * (MT2 * t + mt) + w, G - 1);
+    gt[1] = min(8 * (MT2 * t + mt) + w + 4, G - 1);
   };
   uint64_t* out = FP4 ? p.or_p : p.os_p;
   auto emit = [&](int mt, const f32x4 (&acc)[2]) {
     if (r < nc) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int g = 8 * (MF_MT2 * t + mt) + w + 4 * tt;
+        const int g = 8 * (MT2 * t + mt) + w + 4 * tt;
         if (g < G) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -1514,8 +1587,8 @@ __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
       mf2_load<FP4, FULL>(p, down, gt, 1 % S, bb, 0.f);
     }
   }
-  {  // wait until every FC1 tile of this column group has published its h
-    const int ntile = (K + MF_NT1 - 1) / MF_NT1;
+  {  // wait until every FC1 tile (shared expert: 16-row group) of this column group has published its h
+    const int ntile = FP4 ? (K + MF_NT1 - 1) / MF_NT1 : (K + 15) / 16;
     bool ok = true;
     if ((int)threadIdx.x < ntile) {
       uint64_t f[1];
@@ -1628,7 +1701,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
       build_schedule(p, st, reinterpret_cast<int*>(xs), L.wtot);
       st.x_cached = false;
     } else if ((rel -= p.n_sch) < p.n_s1) {
-      if constexpr (MF) mf_fc1_unit<false, FULL>(p, st, L, mfb, -1, rel / p.mf_t1s, rel % p.mf_t1s);
+      if constexpr (MF) mf_sh1_unit<FULL>(p, st, L, mfb, rel / p.mf_t1s, rel % p.mf_t1s);
       else shared_fc1_unit<RG, FULL>(p, st, L, xs, rel);
     } else {
       rel -= p.n_s1;
@@ -1643,7 +1716,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
           const int gc = rel / p.mf_t1, ae = find_expert(st, gc);
           mf_fc1_unit<true, FULL>(p, st, L, mfb, ae, gc - st.s_cg_off[ae], rel % p.mf_t1);
         } else if ((rel -= NCG * p.mf_t1) < p.n_s2) {
-          mf_fc2_unit<false, FULL>(p, st, L, mfb, -1, rel / p.mf_t2, rel % p.mf_t2);
+          mf_fc2_unit<false, FULL>(p, st, L, mfb, -1, rel / p.mf_t2s, rel % p.mf_t2s);
         } else if ((rel -= p.n_s2) < NCG * p.mf_t2) {
           const int gc = rel / p.mf_t2, ae = find_expert(st, gc);
           mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, gc - st.s_cg_off[ae], rel % p.mf_t2);
@@ -1789,12 +1862,13 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.n_r2 = (a.H + NTR2 - 1) / NTR2;
   p.n_tile = (a.H + NT2 - 1) / NT2;
   p.mf_t1 = (a.I + MF_NT1 - 1) / MF_NT1;
-  p.mf_t1s = (a.Is + MF_NT1 - 1) / MF_NT1;
+  p.mf_t1s = (a.Is + 15) / 16;
   p.mf_t2 = (a.H + MF_NT2 - 1) / MF_NT2;
+  p.mf_t2s = (a.H + 127) / 128;
   p.mf_cgs = (a.B + MF_COLS - 1) / MF_COLS;
   if (a.B > 1) {  // MFMA path: shared expert units per column group
     p.n_s1 = a.Is > 0 ? p.mf_cgs * p.mf_t1s : 0;
-    p.n_s2 = a.Is > 0 ? p.mf_cgs * p.mf_t2 : 0;
+    p.n_s2 = a.Is > 0 ? p.mf_cgs * p.mf_t2s : 0;
   }
   p.cg_off = a.ws.sched.cg_off;
   p.hflag = a.ws.hflag;
