@@ -118,7 +118,8 @@ __device__ __forceinline__ void set_error(const LayerParams& p) {
 // ---- per-workgroup state ------------------------------------------------------
 
 struct Lds {  // static LDS of the kernel
-  int next;        // next unit index
+  int next;        // next unit index (first claim)
+  int nxt[2];      // next unit index, alternating between iterations of the unit loop
   int U;           // distinct experts (once known)
   int wtot[12];    // scan scratch
   int nrows;       // rows of the current unit
@@ -237,7 +238,7 @@ __device__ __forceinline__ void stage_x(const LayerParams& p, WgState& st, const
   const int per_row = p.H / 8;
   for (int i = threadIdx.x; i < nr * per_row; i += 256) {
     const int r = i / per_row, c = i - r * per_row;
-    const int b = routed ? L.slot[g0 + r] / p.k : L.slot[g0 + r];
+    const int b = p.B == 1 ? 0 : (routed ? L.slot[g0 + r] / p.k : L.slot[g0 + r]);
     xs[r * p.xstride + swz(c)] = reinterpret_cast<const u32x4*>(p.x + (size_t)b * p.H)[c];
   }
   __syncthreads();
@@ -686,16 +687,17 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// The h row of slot L.slot[r] (tagged pairs written earlier in this launch),
+// The h row of `slot` (tagged pairs written earlier in this launch),
 // polled until every pair carries this call's tag, into LDS as two bf16
 // rows: hi = bf16(h) and lo = bf16(h - hi), so that hi + lo is h to within
 // about 2^-17 relative.  Element e sits at bf16 (swz(e / 8), e % 8) of each
 // row (8-element granules, the layout of the x row), lo at granule offset hlo.
+// The caller's unit starts right after the unit loop's barrier, so no wave
+// still reads the previous unit's LDS h.
 __device__ __forceinline__ void stage_h_split(const LayerParams& p, const WgState& st, u32x4* hs, const uint64_t* src,
-                                              const Lds& L, int r, int K, int hlo) {
-  __syncthreads();
+                                              int slot, int K, int hlo) {
   uint16_t* h16 = reinterpret_cast<uint16_t*>(hs);
-  const size_t row = (size_t)L.slot[r] * K;
+  const size_t row = (size_t)slot * K;
   bool ok = true;
   for (int base = threadIdx.x; base < K; base += 256 * 8) {
     uint64_t v[8];
@@ -961,14 +963,13 @@ __device__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
 // all of the expert's rows (RG at a time).
 template <int RG, bool FULL>
 __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g) {
-  load_rows(p, st, L, a);
-  const int nrows_unit = L.nrows;
+  // batch 1: active expert a has exactly one row, its slot (no LDS row list, no barrier)
+  const int slot = st.s_rows[st.s_row_off[a]];
   const uint8_t* blob = p.experts + (size_t)st.s_active[a] * p.blob_bytes;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int C1 = p.H / 32, S1 = (C1 + 15) / 16;
   const int P = w < S1 ? (S1 - w + 3) / 4 : 0;
-  for (int g0 = 0; g0 < nrows_unit; g0 += RG) {
-    const int nr = min(RG, nrows_unit - g0);
+  {
     Fc1Tile<RG, FULL> f;
     f.blob = blob;
     f.C1 = C1;
@@ -980,7 +981,7 @@ __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.au = f.ag;
     TileBuf1 ba, bb;
     prime_passes(f, P, ba, bb);
-    stage_x(p, st, L, xs, true, g0, nr);
+    stage_x(p, st, L, xs, true, 0, 1);
     drive_rolling(f, P, ba, bb);
     if ((lane & 15) == 0) {  // column 0: lane 16 q holds rows 4 q .. 4 q + 3
 #pragma unroll
@@ -990,17 +991,17 @@ __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
       }
     }
     __syncthreads();
-    if ((int)threadIdx.x < nr * 16) {
-      const int r = threadIdx.x >> 4, row = threadIdx.x & 15;
+    if ((int)threadIdx.x < 16) {
+      const int r = 0, row = threadIdx.x;
       float vg = 0.0f, vu = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < 4; ++ww) {
         vg += L.red[ww][r][row][0];
         vu += L.red[ww][r][row][1];
       }
-      st_pair_f32(p.hr_p + (size_t)L.slot[g0 + r] * p.I + 16 * g + row, silu_f(vg) * vu, st.tag);
+      st_pair_f32(p.hr_p + (size_t)slot * p.I + 16 * g + row, silu_f(vg) * vu, st.tag);
     }
-    __syncthreads();
+    // L.red is next written by a later unit, after the unit loop's barrier
   }
 }
 
@@ -1038,8 +1039,7 @@ __device__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
 // takes groups 8v + w and 8v + w + 4 and runs one pass per segment along I.
 template <int RG, bool FULL>
 __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v) {
-  load_rows(p, st, L, a);
-  const int nrows_unit = L.nrows;
+  const int slot = st.s_rows[st.s_row_off[a]];  // batch 1: the active expert's one row
   const int C1 = p.H / 32, C2 = p.I / 32, S2 = (C2 + 15) / 16;
   const uint8_t* down = p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * C1 * 17;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -1047,7 +1047,7 @@ __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
   const int ng = g0 < G ? (g0 + 4 < G ? 2 : 1) : 0;
   const int P = ng > 0 ? S2 : 0;
   const int hlo = h_lo_offset(p.I);
-  for (int r0 = 0; r0 < nrows_unit; ++r0) {
+  {
     Fc2Tile<RG, FULL> f;
     f.down = down;
     f.C2 = C2;
@@ -1059,7 +1059,7 @@ __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
     f.acc[1] = f.acc[0];
     TileBuf2 ba, bb;
     prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
-    stage_h_split(p, st, hs, p.hr_p, L, r0, p.I, hlo);
+    stage_h_split(p, st, hs, p.hr_p, slot, p.I, hlo);
     drive_rolling(f, P, ba, bb);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -1068,7 +1068,7 @@ __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
         // column 0 (hi part) plus column 1 (lo part): lanes 16 q and 16 q + 1
         const float val = f.acc[t][i] + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(f.acc[t][i])));
         if ((lane & 15) == 0 && t < ng)
-          st_pair_f32(p.or_p + (size_t)L.slot[r0] * p.H + 16 * (g0 + 4 * t) + 4 * (lane >> 4) + i, val, st.tag);
+          st_pair_f32(p.or_p + (size_t)slot * p.H + 16 * (g0 + 4 * t) + 4 * (lane >> 4) + i, val, st.tag);
       }
     }
   }
@@ -1687,6 +1687,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     __syncthreads();
     u = L.next;
   }
+  int it = 0;
   for (;;) {
     // the next unit is claimed now; its index is only needed after this one
     if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1739,10 +1740,13 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
         }
       }
     }
+    // One barrier per unit: it ends this unit's use of LDS and publishes the
+    // next index.  The index word alternates between two slots, so thread 0
+    // cannot overwrite one that a slower wave has yet to read.
+    if (threadIdx.x == 0) L.nxt[it & 1] = p.n_static + (int)nxt;
     __syncthreads();
-    if (threadIdx.x == 0) L.next = p.n_static + (int)nxt;
-    __syncthreads();
-    u = L.next;
+    u = L.nxt[it & 1];
+    ++it;
   }
   // Exit: the last workgroup out resets the queue and advances the epoch (all
   // other workgroups have made their final control-block access).
