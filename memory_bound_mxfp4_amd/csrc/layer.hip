@@ -88,7 +88,7 @@ struct LayerParams {
   uint64_t* or_p;
   unsigned* ctrl;
   int umax;
-  int n_rt_e;    // router units per row block (batch 1: 4 experts a unit; else 2)
+  int n_rt_e;    // router units per row block (4 experts a unit)
   int n_rb;      // router row blocks
   int n_rt;      // router units = n_rt_e * n_rb
   int n_ro;      // routing units (one per row)
@@ -124,7 +124,7 @@ struct Lds {  // static LDS of the kernel
   int wtot[12];    // scan scratch
   int nrows;       // rows of the current unit
   float gates[MOE_MAX_TOPK];  // combine: gates of the current row
-  float red[4][4][16][2];     // routed FC1: per-wave partial sums [wave][row][tile row][gate/up]
+  alignas(16) float red[4][4][16][2];  // routed FC1: per-wave partial sums [wave][row][tile row][gate/up]; batch > 1 router: [4][32] doubles
   int slot[MAX_ROWS];  // slot ids (routed) or batch rows (shared) of the current unit
 };
 
@@ -848,57 +848,96 @@ __device__ void router_unit(const LayerParams& p, WgState& st, int u) {
   }
 }
 
-// Router unit at batch > 1: experts 2u' and 2u'+1 against a block of 16 rows
-// (u' = u mod pairs, block = u / pairs), so the router matrix is streamed
-// once per 16 rows.  Wave w takes expert 2u' + (w >> 1) and rows 8 (w & 1)
-// .. + 7; lane l takes 8-element chunks c = l, l + 64, ... of the row.  The
-// activation chunks are read straight from global memory: all units read
-// the same few hundred KB of x, which stays in L2, so no LDS staging or
-// barrier is needed and every wave keeps its loads in flight.  Products
-// bf16 x bf16 are exact in fp32 and are summed exactly in fp64.
-__device__ void router_mf_unit(const LayerParams& p, WgState& st, int u) {
-  constexpr int RB = 8;  // rows per wave
-  const int pe = u % p.n_rt_e, blk = u / p.n_rt_e;
+// Sum over the 64 lanes of each of N (a power of two <= 32) per-lane values,
+// reduce-scatter style: at each step a lane keeps half of its values and adds
+// its partner's copy of that half, so N - 1 shuffles (plus 6 - log2 N for the
+// last value) replace 6 per value.  Lane l ends with the total of value
+// (l >> (6 - log2 N)) ... for N 32: value (l >> 1) & 31, held by lanes 2 m and
+// 2 m + 1.
+template <int CNT, int M, int N>
+__device__ __forceinline__ void reduce_scatter_step(double (&v)[N], int lane) {
+  if constexpr (CNT > 1) {
+    const bool up = (lane & M) != 0;
+#pragma unroll
+    for (int i = 0; i < CNT / 2; ++i) {
+      const double recv = __shfl_xor(up ? v[i] : v[i + CNT / 2], M, WAVE);
+      v[i] = (up ? v[i + CNT / 2] : v[i]) + recv;
+    }
+    reduce_scatter_step<CNT / 2, M / 2>(v, lane);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ double reduce_scatter_f64(double (&v)[N]) {
+  static_assert(N >= 1 && N <= 32 && (N & (N - 1)) == 0, "N: a power of two up to 32");
+  const int lane = threadIdx.x & 63;
+  reduce_scatter_step<N, 32>(v, lane);
+  double t = v[0];
+#pragma unroll
+  for (int m = 64 / (2 * N); m >= 1; m >>= 1) t += __shfl_xor(t, m, WAVE);
+  return t;
+}
+
+// Router unit at batch > 1: experts 4 eg .. 4 eg + 3 against rows 8 rb ..
+// 8 rb + 7 (u = rb * groups + eg).  The four waves split K into quarters;
+// lane l takes 8-element chunks l, l + 64, ... of its wave's quarter for all
+// 4 experts and 8 rows, so every activation chunk read from global memory
+// (the few hundred KB of x stay in L2) serves 4 experts (the unit is bound by
+// its fp64 arithmetic, not by these loads).  bf16 values and their
+// products are exact in fp64 and are summed by fp64 FMA (the exact sums the
+// batch-1 router computes); the quarters meet in LDS.
+__device__ void router_mf_unit(const LayerParams& p, WgState& st, Lds& L, int u) {
+  constexpr int RB = 8, EW = 4;  // rows and experts per unit
+  const int eg = u % p.n_rt_e, rb = u / p.n_rt_e;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = min(2 * pe + (w >> 1), p.E - 1);
-  const int b0 = 16 * blk + RB * (w & 1), nr = min(RB, p.B - b0);
-  if (nr <= 0) return;  // wave-uniform: this wave's rows are past the batch
-  const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wr + (size_t)e * p.H);
+  const int e0 = EW * eg, b0 = RB * rb, nr = min(RB, p.B - b0);
+  const int C = p.H / 8, Q = (C + 3) / 4, c_lo = w * Q, c_hi = min(C, c_lo + Q);
+  const int J = (Q + 63) / 64;
+  const u32x4* wr[EW];
+#pragma unroll
+  for (int e = 0; e < EW; ++e) wr[e] = reinterpret_cast<const u32x4*>(p.wr + (size_t)min(e0 + e, p.E - 1) * p.H);
   const u32x4* xr[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) xr[r] = reinterpret_cast<const u32x4*>(p.x + (size_t)(b0 + min(r, nr - 1)) * p.H);
-  double acc[RB];
+  double acc[EW * RB];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) acc[r] = 0.0;
-  const int C = p.H / 8;
-  for (int c = lane; c < C; c += 64) {
-    const u32x4 wv = ld_weight16(wrow + c);
-    u32x4 xv[RB];
+  for (int i = 0; i < EW * RB; ++i) acc[i] = 0.0;
+  for (int j = 0; j < J; ++j) {
+    u32x4 wv[EW], xv[RB];
+    {
+      const int c = min(c_lo + lane + 64 * j, C - 1);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) xv[r] = xr[r][c];
-    float wf[8];
+      for (int e = 0; e < EW; ++e) wv[e] = ld_weight16(wr[e] + c);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      wf[2 * d] = bf16_lo(wv[d]);
-      wf[2 * d + 1] = bf16_hi(wv[d]);
+      for (int r = 0; r < RB; ++r) xv[r] = xr[r][c];
     }
+    const uint32_t msk = (c_lo + lane + 64 * j < c_hi) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      double a = acc[r];
+    for (int d = 0; d < 8; ++d) {
+      double xd[RB], wd[EW];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        a += (double)(wf[2 * d] * bf16_lo(xv[r][d]));
-        a += (double)(wf[2 * d + 1] * bf16_hi(xv[r][d]));
-      }
-      acc[r] = a;
+      for (int r = 0; r < RB; ++r) xd[r] = (double)((d & 1) ? bf16_hi(xv[r][d >> 1]) : bf16_lo(xv[r][d >> 1]));
+#pragma unroll
+      for (int e = 0; e < EW; ++e)
+        wd[e] = (double)((d & 1) ? bf16_hi(wv[e][d >> 1] & msk) : bf16_lo(wv[e][d >> 1] & msk));
+#pragma unroll
+      for (int e = 0; e < EW; ++e)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) acc[e * RB + r] = fma(wd[e], xd[r], acc[e * RB + r]);
     }
   }
-  const double bb = p.bias ? (double)p.bias[e] : 0.0;
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const double v = sum_lanes_f64<64>(acc[r]);
-    if (lane == 0 && r < nr && 2 * pe + (w >> 1) < p.E)
-      st_pair_f32(p.logits_p + (size_t)(b0 + r) * p.E + e, (float)(v + bb), st.tag);
+  const double v = reduce_scatter_f64<EW * RB>(acc);  // lanes 2 m, 2 m + 1: value m = (e, r)
+  double* part = reinterpret_cast<double*>(L.red);   // [4 waves][32]
+  __syncthreads();  // L.red is free (the previous unit is done with it)
+  if ((lane & 1) == 0) part[w * 32 + (lane >> 1)] = v;
+  __syncthreads();
+  if (threadIdx.x < EW * RB) {
+    const int i = threadIdx.x, e = e0 + i / RB, r = i % RB;
+    if (e < p.E && r < nr) {
+      const double bb = p.bias ? (double)p.bias[e] : 0.0;
+      const double t = ((part[i] + part[32 + i]) + part[64 + i]) + part[96 + i];
+      st_pair_f32(p.logits_p + (size_t)(b0 + r) * p.E + e, (float)(t + bb), st.tag);
+    }
   }
 }
 
@@ -1693,7 +1732,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int rel = u;
     if (rel < p.n_rt) {
-      if constexpr (MF) router_mf_unit(p, st, rel);
+      if constexpr (MF) router_mf_unit(p, st, L, rel);
       else router_unit(p, st, rel);
     } else if ((rel -= p.n_rt) < p.n_ro) {
       routing_unit<TPL>(p, st, L, reinterpret_cast<int*>(xs), rel);
@@ -1853,10 +1892,10 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.ctrl = a.ws.ctrl;
   p.umax = a.ws.umax;
   const LaunchShape sh = launch_shape(a.H, a.I, a.E, a.k, a.Is, a.B);
-  p.n_rt_e = a.B > 1 ? (a.E + 1) / 2 : (a.E + 3) / 4;  // batch 1: 4 experts a unit, else 2
+  p.n_rt_e = (a.E + 3) / 4;  // router units per row block: 4 experts each
   p.xstride = sh.xstride;
   p.hstride = sh.hstride;
-  p.n_rb = a.B > 1 ? (a.B + 15) / 16 : (a.B + sh.rg - 1) / sh.rg;  // batch > 1: 16-row router blocks
+  p.n_rb = a.B > 1 ? (a.B + 7) / 8 : 1;  // router row blocks: 8 rows (batch 1: one)
   p.n_rt = p.n_rt_e * p.n_rb;
   p.n_ro = a.B;
   p.n_sch = a.B > 1 ? 1 : 0;

@@ -159,11 +159,6 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m), hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // Max (MAX) or min over each block of `bs` consecutive lanes (bs a power of
 // two, wave-uniform); every lane of a block ends with its block's result.
 template <bool MAX>
