@@ -239,11 +239,15 @@ moe_status moe_decode_layer_timed(const moe_layer_weights* w, const uint16_t* x,
  *                  accumulation; W bf16 [n][k], x bf16 [batch][k], y bf16
  *                  [batch][n]; y must not alias x.  k a multiple of 8.
  * residual_add_bf16: h[b][i] += float(t[b][i]) (h fp32, t bf16).
+ * residual_add_rmsnorm_bf16: residual_add_bf16 then rmsnorm_bf16 of the
+ *                  updated h into out, as one launch (same sums, same order).
  */
 moe_status rmsnorm_bf16(const float* in, int batch, int hidden, float eps, uint16_t* out, void* stream);
 moe_status dense_gemv_bf16(const uint16_t* w, int n, int k, const uint16_t* x, int batch, uint16_t* y,
                            void* stream);
 moe_status residual_add_bf16(float* h, const uint16_t* t, int batch, int hidden, void* stream);
+moe_status residual_add_rmsnorm_bf16(float* h, const uint16_t* t, int batch, int hidden, float eps, uint16_t* out,
+                                     void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);

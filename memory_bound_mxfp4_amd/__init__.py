@@ -25,7 +25,8 @@ MAX_BATCH = 64
 EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size", "router_topk",
            "expert_gemv_mxfp4", "moe_decode_layer", "moe_decode_layer_kernel_count",
            "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "moe_pack_experts",
-           "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "moe_status_string")
+           "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "residual_add_rmsnorm_bf16",
+           "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -71,6 +72,7 @@ def load():
         "rmsnorm_bf16": (I, [P, I, I, F, P, P]),
         "dense_gemv_bf16": (I, [P, I, I, P, I, P, P]),
         "residual_add_bf16": (I, [P, P, I, I, P]),
+        "residual_add_rmsnorm_bf16": (I, [P, P, I, I, F, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -276,3 +278,13 @@ def residual_add_bf16(h, t, stream=None):
     B, H = h.shape
     _check(load().residual_add_bf16(_ptr(h), _ptr(t), B, H, _stream(stream)), "residual_add_bf16")
     return h
+
+
+def residual_add_rmsnorm_bf16(h, t, eps: float = 1e-6, out=None, stream=None):
+    """h += t (in place), then out = bf16(RMSNorm(h)), as one launch."""
+    import torch
+    B, H = h.shape
+    out = torch.empty((B, H), dtype=torch.bfloat16, device=h.device) if out is None else out
+    _check(load().residual_add_rmsnorm_bf16(_ptr(h), _ptr(t), B, H, float(eps), _ptr(out), _stream(stream)),
+           "residual_add_rmsnorm_bf16")
+    return out

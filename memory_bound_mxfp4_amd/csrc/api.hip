@@ -264,6 +264,15 @@ moe_status residual_add_bf16(float* h, const uint16_t* t, int batch, int hidden,
   return MOE_OK;
 }
 
+moe_status residual_add_rmsnorm_bf16(float* h, const uint16_t* t, int batch, int hidden, float eps, uint16_t* out,
+                                     void* stream) {
+  if (!h || !t || !out || batch < 1 || batch > MOE_MAX_BATCH || hidden < 1 || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (launch_residual_add_rmsnorm(h, t, batch, hidden, eps, out, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";

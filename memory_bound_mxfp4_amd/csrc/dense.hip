@@ -11,8 +11,61 @@
 namespace moe {
 
 // out[b] = bf16( in[b] * rsqrt(mean(in[b]^2) + eps) ).  grid: B blocks x 256.
+// Each thread requests its whole share of the row (16-byte chunks, up to
+// RN of them: all of a 7168-element row) before summing, and keeps it in
+// registers for the output pass, so a row costs one memory round trip.
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ in, int H, float eps,
                                                  uint16_t* __restrict__ out) {
+  constexpr int RN = 8;
+  __shared__ float part[4];
+  const int b = blockIdx.x;
+  const float* row = in + (size_t)b * H;
+  const int H4 = H / 4;  // H is a multiple of 4 and the rows are 16-byte aligned on this path
+  f32x4 v[RN];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    v[i] = c < H4 ? reinterpret_cast<const f32x4*>(row)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  for (int c = threadIdx.x + 256 * RN; c < H4; c += 256) {  // rows longer than 256 * RN * 4
+    const f32x4 u = reinterpret_cast<const f32x4*>(row)[c];
+    ss = fmaf(u.x, u.x, fmaf(u.y, u.y, fmaf(u.z, u.z, fmaf(u.w, u.w, ss))));
+  }
+  ss = sum_lanes<64>(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  uint16_t* o = out + (size_t)b * H;
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < H4) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(v[i].x * r) | ((uint32_t)f32_to_bf16(v[i].y * r) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(v[i].z * r) | ((uint32_t)f32_to_bf16(v[i].w * r) << 16);
+      reinterpret_cast<u32x2*>(o)[c] = u32x2{lo, hi};
+    }
+  }
+  for (int c = threadIdx.x + 256 * RN; c < H4; c += 256) {
+    const f32x4 u = reinterpret_cast<const f32x4*>(row)[c];
+    const uint32_t lo = (uint32_t)f32_to_bf16(u.x * r) | ((uint32_t)f32_to_bf16(u.y * r) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(u.z * r) | ((uint32_t)f32_to_bf16(u.w * r) << 16);
+    reinterpret_cast<u32x2*>(o)[c] = u32x2{lo, hi};
+  }
+}
+
+// The same for rows that are not 16-byte aligned (hidden % 4 != 0 or an
+// unaligned buffer): scalar loads, two passes.
+__global__ __launch_bounds__(256) void k_rmsnorm_scalar(const float* __restrict__ in, int H, float eps,
+                                                        uint16_t* __restrict__ out) {
   __shared__ float part[4];
   const int b = blockIdx.x;
   const float* row = in + (size_t)b * H;
@@ -27,7 +80,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ in, i
 }
 
 hipError_t launch_rmsnorm(const float* in, int B, int H, float eps, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(256), 0, s, in, H, eps, out);
+  if (H % 4 == 0 && reinterpret_cast<uintptr_t>(in) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0)
+    hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(256), 0, s, in, H, eps, out);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_scalar, dim3(B), dim3(256), 0, s, in, H, eps, out);
   return hipGetLastError();
 }
 
@@ -109,6 +165,70 @@ __global__ __launch_bounds__(256) void k_residual_add(float* __restrict__ h, con
 hipError_t launch_residual_add(float* h, const uint16_t* t, int B, int H, hipStream_t s) {
   size_t n = (size_t)B * H;
   hipLaunchKernelGGL(k_residual_add, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, t, n);
+  return hipGetLastError();
+}
+
+// Fused residual add and RMSNorm: h[b] += float(t[b]) (fp32, written back),
+// then out[b] = bf16( h[b] * rsqrt(mean(h[b]^2) + eps) ), in one pass of one
+// block per row (the row stays in registers); the same sums, in the same
+// order, as residual_add followed by k_rmsnorm.  Rows 16-byte aligned,
+// hidden a multiple of 4 and at most 256 * 8 * 4.
+__global__ __launch_bounds__(256) void k_residual_add_rmsnorm(float* __restrict__ h, const uint16_t* __restrict__ t,
+                                                              int H, float eps, uint16_t* __restrict__ out) {
+  constexpr int RN = 8;
+  __shared__ float part[4];
+  const int b = blockIdx.x;
+  float* row = h + (size_t)b * H;
+  const uint16_t* trow = t + (size_t)b * H;
+  const int H4 = H / 4;
+  f32x4 v[RN];
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < H4) {
+      const f32x4 a = reinterpret_cast<const f32x4*>(row)[c];
+      const u32x2 tb = reinterpret_cast<const u32x2*>(trow)[c];
+      v[i] = f32x4{a.x + __uint_as_float(tb.x << 16), a.y + __uint_as_float(tb.x & 0xFFFF0000u),
+                   a.z + __uint_as_float(tb.y << 16), a.w + __uint_as_float(tb.y & 0xFFFF0000u)};
+      reinterpret_cast<f32x4*>(row)[c] = v[i];
+    } else {
+      v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    ss = fmaf(v[i].x, v[i].x, ss);
+    ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss);
+    ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = sum_lanes<64>(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  uint16_t* o = out + (size_t)b * H;
+#pragma unroll
+  for (int i = 0; i < RN; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < H4) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(v[i].x * r) | ((uint32_t)f32_to_bf16(v[i].y * r) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(v[i].z * r) | ((uint32_t)f32_to_bf16(v[i].w * r) << 16);
+      reinterpret_cast<u32x2*>(o)[c] = u32x2{lo, hi};
+    }
+  }
+}
+
+hipError_t launch_residual_add_rmsnorm(float* h, const uint16_t* t, int B, int H, float eps, uint16_t* out,
+                                       hipStream_t s) {
+  const bool fused = H % 4 == 0 && H <= 256 * 8 * 4 && reinterpret_cast<uintptr_t>(h) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(t) % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
+  if (!fused) {  // two passes: the add, then the norm
+    hipError_t e = launch_residual_add(h, t, B, H, s);
+    return e != hipSuccess ? e : launch_rmsnorm(h, B, H, eps, out, s);
+  }
+  hipLaunchKernelGGL(k_residual_add_rmsnorm, dim3(B), dim3(256), 0, s, h, t, H, eps, out);
   return hipGetLastError();
 }
 

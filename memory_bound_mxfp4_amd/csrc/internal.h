@@ -94,6 +94,8 @@ hipError_t launch_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int N,
 hipError_t launch_rmsnorm(const float* in, int B, int H, float eps, uint16_t* out, hipStream_t s);
 hipError_t launch_dense_gemv(const uint16_t* w, int N, int K, const uint16_t* x, int B, uint16_t* y, hipStream_t s);
 hipError_t launch_residual_add(float* h, const uint16_t* t, int B, int H, hipStream_t s);
+hipError_t launch_residual_add_rmsnorm(float* h, const uint16_t* t, int B, int H, float eps, uint16_t* out,
+                                       hipStream_t s);
 
 int num_cus();
 

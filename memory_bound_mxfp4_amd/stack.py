@@ -4,8 +4,8 @@ Per layer l (batch rows b, fp32 residual stream h):
 
     n = bf16(RMSNorm(h))                      eps 1e-6, gain 1
     t = n; for each of the layer's dense matrices W: t = bf16(W t)
-    h += t
-    x = bf16(RMSNorm(h))
+    h += t                                    } one launch
+    x = bf16(RMSNorm(h))                      }
     h = moe_decode_layer_l(x, residual = h)
 
 This is the shape of one decode step of the model described in "Kimi K3 on
@@ -67,8 +67,7 @@ class DecodeStack:
                 t = y
                 if record is not None:
                     chain.append(y.clone())
-            moe.residual_add_bf16(h, t, stream=stream)
-            moe.rmsnorm_bf16(h, self.eps, out=self.x, stream=stream)
+            moe.residual_add_rmsnorm_bf16(h, t, self.eps, out=self.x, stream=stream)
             if record is not None:
                 rec.update(n=self.n.clone(), chain=chain, h_mid=h.clone(), x=self.x.clone())
             moe.moe_decode_layer(w, self.x, h, idx=self.idx[l], gate=self.gate[l], ws=self.ws, stream=stream)

@@ -107,3 +107,9 @@ def test_dense_pieces_match_oracle():
     moe.residual_add_bf16(hh, _dev(t))
     ref = h + (t.astype(np.uint32) << 16).view(np.float32)
     assert np.array_equal(hh.cpu().numpy(), ref)
+    # the fused add + norm equals the two launches bit for bit
+    h2 = _dev(h.copy())
+    x2 = moe.residual_add_rmsnorm_bf16(h2, _dev(t), 1e-6)
+    assert np.array_equal(h2.cpu().numpy(), ref)
+    x1 = moe.rmsnorm_bf16(hh, 1e-6)
+    assert torch.equal(x1, x2)
