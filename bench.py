@@ -130,9 +130,12 @@ CALIB_BYTES = 256 << 20  # plain device-to-device copy used to scale the HBM byt
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the sources the layer kernel is compiled from."""
+    """sha256 over the sources the layer kernel is compiled from and the
+    compiler flags it is built with."""
     import hashlib
+    from memory_bound_mxfp4_amd import build as _build
     h = hashlib.sha256()
+    h.update(" ".join(_build.FLAGS).encode())
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "memory_bound_mxfp4_amd", "csrc", name), "rb") as f:
             h.update(f.read())

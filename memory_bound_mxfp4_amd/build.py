@@ -9,9 +9,13 @@ ROOT = os.path.dirname(PKG)
 SO = os.path.join(PKG, "libmoe_mxfp4.so")
 SOURCES = ["api.hip", "router.hip", "experts.hip", "dense.hip", "pack.hip", "layer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU ops are disabled for all device code.
+# Packed fp32 VALU ops are disabled for all device code.  The atomic
+# optimizer is off: it rewrites a one-lane atomic into a wave-wide pattern
+# whose result is broadcast straight away, which makes every work-queue pop
+# wait for its round trip before the unit's own loads can issue.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def build(verbose: bool = False) -> str:
