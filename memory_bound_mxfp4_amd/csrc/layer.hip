@@ -1275,6 +1275,16 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
   if (FP4) {
     const int C1 = p.H / 32;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
+    // B fragments are read from LDS two steps ahead; each read is tied to
+    // the accumulator of the step before, so the compiler cannot hoist all
+    // sixteen (and spill) but the read latency overlaps two steps of MFMAs.
+    auto rd = [&](int i) {
+      const int kb = i >> 2, d = i & 3, c = 4 * kb + q;
+      return *reinterpret_cast<const u32x4*>(xb + after(xoff + (128 * kb + 32 * q + 8 * (FULL || c < SC ? d : 0)) * 2, ag[0]));
+    };
+    u32x4 xr[16];
+    xr[0] = rd(0);
+    xr[1] = rd(1);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int c = 4 * kb + q;
@@ -1283,8 +1293,9 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
       const float su = e8m0_scale(tile_scale<FULL>(b.s[1], kb, q));
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(xb + after(xoff + (128 * kb + 32 * q + 8 * (FULL || c < SC ? d : 0)) * 2, ag[0]));
-        const bf16x8 xv = __builtin_bit_cast(bf16x8, (live && (FULL || c < SC)) ? raw : z);
+        const int i = 4 * kb + d;
+        if (i + 2 < 16) xr[i + 2] = rd(i + 2);
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, (live && (FULL || c < SC)) ? xr[i] : z);
         ag = mfma_bf16(fp4x8_bf16(b.q[0][kb][d] & msk, sg), xv, ag);
         au = mfma_bf16(fp4x8_bf16(b.q[1][kb][d] & msk, su), xv, au);
       }
@@ -1495,6 +1506,17 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
   if (FP4) {
     const int C2 = p.I / 32;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
+    // h fragments are read from LDS two steps ahead (see mf1_math)
+    u32x4 rh[16], rl[16];
+    auto rd = [&](int i) {
+      const int kb = i >> 2, d = i & 3, c = 4 * kb + q;
+      const bool bv = live && (FULL || c < SC);
+      const int off = after(hoff + (bv ? (128 * kb + 32 * q + 8 * d) * 2 : 0), acc[0][0] + acc[1][0]);
+      rh[i] = *reinterpret_cast<const u32x4*>(hb + off);
+      rl[i] = *reinterpret_cast<const u32x4*>(lob + off);
+    };
+    rd(0);
+    rd(1);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int c = 4 * kb + q;
@@ -1504,12 +1526,11 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
       for (int t = 0; t < 2; ++t) sc[t] = e8m0_scale(tile_scale<FULL>(b.s[t], kb, q));
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
+        const int i = 4 * kb + d;
+        if (i + 2 < 16) rd(i + 2);
         const bool bv = live && (FULL || c < SC);
-        const int off = after(hoff + (bv ? (128 * kb + 32 * q + 8 * d) * 2 : 0), acc[0][0] + acc[1][0]);
-        const u32x4 rh = *reinterpret_cast<const u32x4*>(hb + off);
-        const u32x4 rl = *reinterpret_cast<const u32x4*>(lob + off);
-        const bf16x8 hi = __builtin_bit_cast(bf16x8, bv ? rh : z);
-        const bf16x8 lo = __builtin_bit_cast(bf16x8, bv ? rl : z);
+        const bf16x8 hi = __builtin_bit_cast(bf16x8, bv ? rh[i] : z);
+        const bf16x8 lo = __builtin_bit_cast(bf16x8, bv ? rl[i] : z);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const bf16x8 wv = fp4x8_bf16(b.q[t][kb][d] & msk, sc[t]);
@@ -1583,10 +1604,9 @@ __device__ __forceinline__ void mf_stage_h(const LayerParams& p, const Lds& L, c
 // (FP4) or the shared expert (a < 0), column group cg, once every FC1 tile of
 // that column group is done.  A narrow column group stages all of h once and
 // runs one pipelined pass per (tile, segment) with no barrier; a wide one
-// stages h per segment.
+// stages h 512 elements at a time.
 template <bool FP4, bool FULL>
 __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
-  constexpr int KS = FP4 ? 512 : 128;
   load_cols(p, st, L, a, cg);
   const int nc = L.nrows;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
@@ -1615,15 +1635,18 @@ __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
       }
     }
   };
-  const int P = MT * S;  // passes: (tile, segment) pairs
   MfBuf ba, bb;
-  {  // the weights do not depend on FC1
+  const int XF = K * 2 + 16;  // column stride of whole-K staging
+  const bool narrow = 2 * nc * XF <= MF_STAGE_BYTES;
+  {  // the weights do not depend on FC1.  The second pass is tile 1 at
+     // segment 0 on the wide FP4 path (chunk order), else tile 0 at segment 1.
     int gt[2];
     groups(0, gt);
     mf2_load<FP4, FULL>(p, down, gt, 0, ba, 0.f);
-    if (P > 1) {
-      groups(1 / S, gt);
-      mf2_load<FP4, FULL>(p, down, gt, 1 % S, bb, 0.f);
+    const bool by_tile = FP4 && !narrow;
+    if (by_tile ? MT > 1 : MT * S > 1) {
+      groups(by_tile ? 1 : 1 / S, gt);
+      mf2_load<FP4, FULL>(p, down, gt, by_tile ? 0 : 1 % S, bb, 0.f);
     }
   }
   {  // wait until every FC1 tile (shared expert: 16-row group) of this column group has published its h
@@ -1638,11 +1661,12 @@ __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
     if (!ok) set_error(p);
   }
   const float* hsrc = FP4 ? reinterpret_cast<const float*>(p.hr_p) : reinterpret_cast<const float*>(p.hs_p);
-  const int XF = K * 2 + 16;  // column stride of whole-K staging
-  const bool live = r < nc;
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const f32x4 zero4{0.f, 0.f, 0.f, 0.f};
-  if (2 * nc * XF <= MF_STAGE_BYTES) {
+  if (narrow) {  // all of h staged once; passes tile by tile
+    constexpr int KS = FP4 ? 512 : 128;
+    const int P = MT * S;
+    const bool live = r < nc;
+    f32x4 acc[2] = {zero4, zero4};
     __syncthreads();
     mf_stage_h<16>(p, L, hsrc, K, 0, K, nc, nc, mfb, XF, nc * XF);
     __syncthreads();
@@ -1669,31 +1693,41 @@ __device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
       }
     }
   } else {
-    constexpr int XS = KS * 2 + 16;
-    for (int pp = 0; pp < P; pp += 2) {
+    // Wide column group: h goes through LDS 512 elements at a time (hi and lo
+    // halves fill the staging region), and every pass that reads a chunk runs
+    // while it is staged, so a unit stages h K / 512 times instead of once per
+    // (tile, segment).  Pass (c, j) is FP4 tile j at segment c, or bf16 tile 0
+    // at segment 4 c + j; four passes a chunk keep the two weight buffers
+    // alternating.
+    constexpr int XS = 512 * 2 + 16;
+    const int NCH = (K + 511) / 512;
+    f32x4 accs[MT2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ps = pp + h;
-        if (ps < P) {
-          const int mt = ps / S, sg = ps - mt * S;
-          __syncthreads();  // the previous segment's h is no longer read
-          mf_stage_h<KS / 32>(p, L, hsrc, K, sg * KS, KS, nc, MF_COLS, mfb, XS, MF_COLS * XS);
-          __syncthreads();
-          MfBuf& b = h ? bb : ba;
-          mf2_math<FP4, FULL>(p, sg, b, mfb + r * XS, mfb + MF_COLS * XS + r * XS, 0, true, acc);
-          if (ps + 2 < P) {
-            int gt[2];
-            groups((ps + 2) / S, gt);
-            mf2_load<FP4, FULL>(p, down, gt, (ps + 2) % S, b, acc[0][0] + acc[1][0]);
-          }
-          if (sg == S - 1) {
-            emit(mt, acc);
-            acc[0] = zero4;
-            acc[1] = zero4;
-          }
+    for (int i = 0; i < MT2; ++i) accs[i][0] = accs[i][1] = zero4;
+    auto seg_of = [&](int c, int j) { return FP4 ? c : 4 * c + j; };
+    auto pass_ok = [&](int c, int j) { return c < NCH && seg_of(c, j) < S && (FP4 ? j < MT : true); };
+    for (int c = 0; c < NCH; ++c) {
+      __syncthreads();  // the previous chunk's h is no longer read
+      mf_stage_h<16>(p, L, hsrc, K, c * 512, 512, nc, MF_COLS, mfb, XS, MF_COLS * XS);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        MfBuf& b = (j & 1) ? bb : ba;
+        f32x4 (&acc_j)[2] = accs[FP4 ? j % MT2 : 0];
+        if (pass_ok(c, j))
+          mf2_math<FP4, FULL>(p, seg_of(c, j), b, mfb + r * XS, mfb + MF_COLS * XS + r * XS, FP4 ? 0 : j * 256, true,
+                              acc_j);
+        const int c2 = j + 2 < 4 ? c : c + 1, j2 = j + 2 < 4 ? j + 2 : j - 2;
+        if (pass_ok(c2, j2)) {
+          int gt[2];
+          groups(FP4 ? j2 : 0, gt);
+          mf2_load<FP4, FULL>(p, down, gt, seg_of(c2, j2), b, acc_j[0][0] + acc_j[1][0]);
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < MT2; ++i)
+      if (i < MT) emit(i, accs[i]);
   }
 }
 
