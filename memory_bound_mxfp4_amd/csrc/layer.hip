@@ -160,7 +160,7 @@ __device__ __forceinline__ uint32_t poll_ready(const LayerParams& p, uint32_t ta
 // "active expert" j with row list {j}; its expert comes from the routing
 // pairs.  Batch > 1: wait for the schedule unit's ready word, then copy the
 // published schedule (one batch of coherent loads).
-__device__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* sc) {
+__device__ __forceinline__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* sc) {
   int* a = sc;
   int* ro = sc + p.umax;
   int* rw = ro + p.umax + 1;
@@ -723,7 +723,7 @@ __device__ __forceinline__ void stage_h_split(const LayerParams& p, const WgStat
 
 // Expert-gathered schedule from the routing pairs of all B*k slots (LDS
 // counting; 256 threads).  LDS: cnt[E], start[E], ids[B*k].
-__device__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt, int* wtot /* LDS [8] */) {
+__device__ __forceinline__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt, int* wtot /* LDS [8] */) {
   int* start = cnt + p.E;
   int* ids = start + p.E;
   const int t = threadIdx.x, nslots = p.B * p.k;
@@ -814,7 +814,7 @@ __device__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt
 // the launch's workgroups -- the first workgroup of each CU, which starts
 // streaming before the CU's second one.  bf16 x bf16 products are exact in
 // fp32 and are summed in fp64.
-__device__ void router_unit(const LayerParams& p, WgState& st, int u) {
+__device__ __forceinline__ void router_unit(const LayerParams& p, WgState& st, int u) {
   constexpr int NG = 14;  // granules in flight per lane: a whole row at H 7168
   const int lane = threadIdx.x & 63;
   const int e = 4 * u + (threadIdx.x >> 6);
@@ -886,7 +886,7 @@ __device__ __forceinline__ double reduce_scatter_f64(double (&v)[N]) {
 // its fp64 arithmetic, not by these loads).  bf16 values and their
 // products are exact in fp64 and are summed by fp64 FMA (the exact sums the
 // batch-1 router computes); the quarters meet in LDS.
-__device__ void router_mf_unit(const LayerParams& p, WgState& st, Lds& L, int u) {
+__device__ __forceinline__ void router_mf_unit(const LayerParams& p, WgState& st, Lds& L, int u) {
   constexpr int RB = 8, EW = 4;  // rows and experts per unit
   const int eg = u % p.n_rt_e, rb = u / p.n_rt_e;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -946,7 +946,7 @@ __device__ void router_mf_unit(const LayerParams& p, WgState& st, Lds& L, int u)
 // region): holding it in registers would set the register budget -- and so
 // the occupancy -- of the whole kernel.
 template <int TPL>
-__device__ void routing_unit(const LayerParams& p, WgState& st, Lds& L, int* lds_ints, int b) {
+__device__ __forceinline__ void routing_unit(const LayerParams& p, WgState& st, Lds& L, int* lds_ints, int b) {
   __builtin_amdgcn_s_setprio(3);  // on the critical path: issue ahead of streaming waves
   const size_t s0 = (size_t)b * p.k;
   uint32_t* cand = reinterpret_cast<uint32_t*>(lds_ints);
@@ -969,7 +969,7 @@ __device__ void routing_unit(const LayerParams& p, WgState& st, Lds& L, int* lds
 }
 
 template <int RG, bool FULL>
-__device__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int t) {
+__device__ __forceinline__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int t) {
   const int n_begin = t * NTS1, n_end = min(p.Is, n_begin + NTS1);
   const int half = (threadIdx.x & 63) >> 5;
   load_rows(p, st, L, -1);
@@ -1001,7 +1001,7 @@ __device__ void shared_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
 // Routed FC1 + SwiGLU of row group g (16 rows of I) of active expert a, for
 // all of the expert's rows (RG at a time).
 template <int RG, bool FULL>
-__device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g) {
+__device__ __forceinline__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g) {
   // batch 1: active expert a has exactly one row, its slot (no LDS row list, no barrier)
   const int slot = st.s_rows[st.s_row_off[a]];
   const uint8_t* blob = p.experts + (size_t)st.s_active[a] * p.blob_bytes;
@@ -1045,7 +1045,7 @@ __device__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
 }
 
 template <int RG, bool FULL>
-__device__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int v) {
+__device__ __forceinline__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int v) {
   const int m_begin = v * NTS2, m_end = min(p.H, m_begin + NTS2);
   load_rows(p, st, L, -1);
   for (int g0 = 0; g0 < p.B; g0 += RG) {
@@ -1077,7 +1077,7 @@ __device__ void shared_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
 // Routed FC2 of 8 row groups (128 rows of H) of active expert a: wave w
 // takes groups 8v + w and 8v + w + 4 and runs one pass per segment along I.
 template <int RG, bool FULL>
-__device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v) {
+__device__ __forceinline__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v) {
   const int slot = st.s_rows[st.s_row_off[a]];  // batch 1: the active expert's one row
   const int C1 = p.H / 32, C2 = p.I / 32, S2 = (C2 + 15) / 16;
   const uint8_t* down = p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * C1 * 17;
@@ -1116,7 +1116,7 @@ __device__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4
 // Combine unit (row b, tile t of NT2 rows of H): residual += shared output +
 // sum_j gate_j * o_j in fixed j order, polling the outputs until they are
 // this call's.  Thread i owns row m = t*NT2 + i.
-__device__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, int t) {
+__device__ __forceinline__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, int t) {
   __syncthreads();
   const size_t s0 = (size_t)b * p.k;
   if (threadIdx.x < p.k) {
@@ -1176,6 +1176,7 @@ constexpr int MF_NT2 = 128 * MF_MT2;  // FC2 rows of H per unit
 constexpr int MF_XS_FP4 = 512 * 2 + 16;  // LDS column stride (bytes) of a 512-element segment
 constexpr int MF_XS_BF = 128 * 2 + 16;   // ... of a 128-element segment (bf16 weights)
 constexpr int MF_STAGE_BYTES = 2 * MF_COLS * MF_XS_FP4;  // LDS staging region of the MFMA units
+constexpr int MF_LA = 3;  // MFMA steps between an LDS read of a B fragment and its use
 
 // Column list of a unit: batch rows 16 cg .. of the shared expert (a < 0),
 // or rows 16 cg .. of active expert a's row list (slot ids).
@@ -1275,16 +1276,16 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
   if (FP4) {
     const int C1 = p.H / 32;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
-    // B fragments are read from LDS two steps ahead; each read is tied to
+    // B fragments are read from LDS MF_LA steps ahead; each read is tied to
     // the accumulator of the step before, so the compiler cannot hoist all
-    // sixteen (and spill) but the read latency overlaps two steps of MFMAs.
+    // sixteen (and spill) but the read latency overlaps MF_LA steps of MFMAs.
     auto rd = [&](int i) {
       const int kb = i >> 2, d = i & 3, c = 4 * kb + q;
       return *reinterpret_cast<const u32x4*>(xb + after(xoff + (128 * kb + 32 * q + 8 * (FULL || c < SC ? d : 0)) * 2, ag[0]));
     };
     u32x4 xr[16];
-    xr[0] = rd(0);
-    xr[1] = rd(1);
+#pragma unroll
+    for (int i = 0; i < MF_LA; ++i) xr[i] = rd(i);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int c = 4 * kb + q;
@@ -1294,7 +1295,7 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int i = 4 * kb + d;
-        if (i + 2 < 16) xr[i + 2] = rd(i + 2);
+        if (i + MF_LA < 16) xr[i + MF_LA] = rd(i + MF_LA);
         const bf16x8 xv = __builtin_bit_cast(bf16x8, (live && (FULL || c < SC)) ? xr[i] : z);
         ag = mfma_bf16(fp4x8_bf16(b.q[0][kb][d] & msk, sg), xv, ag);
         au = mfma_bf16(fp4x8_bf16(b.q[1][kb][d] & msk, su), xv, au);
@@ -1315,7 +1316,7 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
 // FC1 + SwiGLU of rows [64 t, 64 t + 64) (wave w: row group 4 t + w) of the
 // routed expert a (FP4) or the shared expert (bf16, a < 0), column group cg.
 template <bool FP4, bool FULL>
-__device__ void mf_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
+__device__ __forceinline__ void mf_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
   constexpr int KS = FP4 ? 512 : 128, XS = KS * 2 + 16;
   load_cols(p, st, L, a, cg);
   const int nc = L.nrows;
@@ -1408,7 +1409,7 @@ __device__ void mf_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb
 // stream.  Partial sums meet in LDS; h goes out as fp32 with coherent stores,
 // then the group's "done" flag (after every store has completed).
 template <bool FULL>
-__device__ void mf_sh1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int cg, int g) {
+__device__ __forceinline__ void mf_sh1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int cg, int g) {
   load_cols(p, st, L, -1, cg);
   const int nc = L.nrows;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
@@ -1506,7 +1507,7 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
   if (FP4) {
     const int C2 = p.I / 32;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
-    // h fragments are read from LDS two steps ahead (see mf1_math)
+    // h fragments are read from LDS MF_LA steps ahead (see mf1_math)
     u32x4 rh[16], rl[16];
     auto rd = [&](int i) {
       const int kb = i >> 2, d = i & 3, c = 4 * kb + q;
@@ -1515,8 +1516,8 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
       rh[i] = *reinterpret_cast<const u32x4*>(hb + off);
       rl[i] = *reinterpret_cast<const u32x4*>(lob + off);
     };
-    rd(0);
-    rd(1);
+#pragma unroll
+    for (int i = 0; i < MF_LA; ++i) rd(i);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int c = 4 * kb + q;
@@ -1527,7 +1528,7 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int i = 4 * kb + d;
-        if (i + 2 < 16) rd(i + 2);
+        if (i + MF_LA < 16) rd(i + MF_LA);
         const bool bv = live && (FULL || c < SC);
         const bf16x8 hi = __builtin_bit_cast(bf16x8, bv ? rh[i] : z);
         const bf16x8 lo = __builtin_bit_cast(bf16x8, bv ? rl[i] : z);
@@ -1606,7 +1607,7 @@ __device__ __forceinline__ void mf_stage_h(const LayerParams& p, const Lds& L, c
 // runs one pipelined pass per (tile, segment) with no barrier; a wide one
 // stages h 512 elements at a time.
 template <bool FP4, bool FULL>
-__device__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
+__device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
   load_cols(p, st, L, a, cg);
   const int nc = L.nrows;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
