@@ -145,7 +145,45 @@ __global__ __launch_bounds__(256) void k_dense_gemv(const uint16_t* __restrict__
   }
 }
 
+// One activation row (batch 1): half a wave per weight row, and the x
+// granules read from global memory beside the weight granules (the 14 KB row
+// stays in L2), so no staging round trip and no barrier precede the weight
+// loads.  NB granules of each are requested before any is used.
+template <int NB>
+__global__ __launch_bounds__(256) void k_dense_gemv1(const uint16_t* __restrict__ w, int N, int K,
+                                                     const uint16_t* __restrict__ x, uint16_t* __restrict__ y) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const int n = blockIdx.x * 8 + wave * 2 + half;
+  const int C8 = K / 8;
+  const uint16_t* wr = w + (size_t)min(n, N - 1) * K;
+  float acc = 0.0f;
+  for (int c0 = l32; c0 < C8; c0 += 32 * NB) {
+    u32x4 q[NB], xv[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int c = min(c0 + 32 * i, C8 - 1);
+      q[i] = ld_weight16(wr + 8 * (size_t)c);
+      xv[i] = ld16(x + 8 * (size_t)c);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (c0 + 32 * i < C8) {
+        acc = dot2_bf16(q[i][0], xv[i][0], acc);
+        acc = dot2_bf16(q[i][1], xv[i][1], acc);
+        acc = dot2_bf16(q[i][2], xv[i][2], acc);
+        acc = dot2_bf16(q[i][3], xv[i][3], acc);
+      }
+    }
+  }
+  const float v = sum_lanes<32>(acc);
+  if (l32 == 0 && n < N) y[n] = f32_to_bf16(v);
+}
+
 hipError_t launch_dense_gemv(const uint16_t* w, int N, int K, const uint16_t* x, int B, uint16_t* y, hipStream_t s) {
+  if (B == 1 && reinterpret_cast<uintptr_t>(x) % 16 == 0) {
+    hipLaunchKernelGGL(k_dense_gemv1<14>, dim3((N + 7) / 8), dim3(256), 0, s, w, N, K, x, y);
+    return hipGetLastError();
+  }
   size_t row_bytes = (size_t)K * 2;
   int rg = B <= 1 ? 1 : (B <= 2 ? 2 : 4);
   while (rg > 1 && rg * row_bytes > 65536) rg >>= 1;
