@@ -130,7 +130,8 @@ moe_status moe_workspace_size(const moe_layer_weights* w, int batch, size_t* byt
  * rows x 16 scale blocks (16 x 512 elements; the last tile of a row group
  * holds the remaining K/32 mod 16 blocks).  A tile of SC blocks holds its
  * codes as [SC][16 rows] x 16 bytes followed by its scales as [16 rows][SC]
- * bytes; a row group's tiles are consecutive.  The blob holds, for every
+ * bytes (in a full tile, SC = 16, a row's scale of block 4 kb + q sits at
+ * byte 4 q + kb of the row's 16); a row group's tiles are consecutive.  The blob holds, for every
  * 16-row group of the gate/up rows and every segment along H, the gate tile
  * then the up tile; then the down tiles (16-row groups of H, segments along
  * I); then zero padding up to moe_expert_bytes.  So a wave of 64 lanes reads

@@ -451,35 +451,42 @@ struct TileBuf2 {  // one FC2 segment of two row groups
   u32x4 s[2];
 };
 
-// Scale byte of block 4 kb + q of this lane's row: FULL tiles hold the row's
-// 16 scale bytes as one 16-byte vector; partial tiles gather the 4 bytes the
-// lane needs into the first dword (byte kb).
-template <bool FULL>
-__device__ __forceinline__ uint32_t tile_scale(const u32x4& v, int kb, int q) {
-  return FULL ? (v[kb] >> (8 * q)) & 0xFFu : (v[0] >> (8 * kb)) & 0xFFu;
+// A lane (16 q + r) decodes blocks 4 kb + q (kb = 0..3) of row r of a tile,
+// and holds their four scale bytes as one dword, byte kb.  A full tile
+// stores each row's scales so that this dword is one aligned load (block
+// 4 kb + q at byte 4 q + kb of the row); a partial tile's are gathered.
+__device__ __forceinline__ uint32_t tile_scale(uint32_t v, int kb) { return (v >> (8 * kb)) & 0xFFu; }
+
+// Byte offset, in a tile's scale area, of block c of row r (SC blocks).
+__device__ __forceinline__ int scale_pos(int SC, int r, int c) {
+  return SC == 16 ? r * 16 + (c & 3) * 4 + (c >> 2) : r * SC + c;
+}
+
+__device__ __forceinline__ uint32_t ld_weight4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
 template <bool FULL>
-__device__ __forceinline__ void load_tile(const uint8_t* t, int SC, u32x4 (&cq)[4], u32x4& sv) {
+__device__ __forceinline__ void load_tile(const uint8_t* t, int SC, u32x4 (&cq)[4], uint32_t& sv) {
   const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
   if (FULL) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) cq[kb] = ld_weight16(t + kb * 1024 + l * 16);
-    sv = ld_weight16(t + 4096 + r * 16);
+    sv = ld_weight4(t + 4096 + r * 16 + q * 4);
   } else {
     uint32_t b = 0;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int c = min(4 * kb + q, SC - 1);
       cq[kb] = ld_weight16(t + c * 256 + r * 16);
-      b |= (uint32_t)t[SC * 256 + r * SC + c] << (8 * kb);
+      b |= (uint32_t)t[SC * 256 + scale_pos(SC, r, c)] << (8 * kb);
     }
-    sv = u32x4{b, 0u, 0u, 0u};
+    sv = b;
   }
 }
 
 // One 1 KB slab kb of a tile's codes (lane 16 q + r: block 4 kb + q of row
-// r), and the tile's scale vector, as load_tile reads them.
+// r), and the tile's scale dword, as load_tile reads them.
 template <bool FULL>
 __device__ __forceinline__ u32x4 load_slab(const uint8_t* t, int SC, int kb) {
   const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
@@ -487,14 +494,48 @@ __device__ __forceinline__ u32x4 load_slab(const uint8_t* t, int SC, int kb) {
   return ld_weight16(t + min(4 * kb + q, SC - 1) * 256 + r * 16);
 }
 
+// The batch-1 streams hold a row's 16 scale bytes as one vector (FULL: as
+// stored; partial: the lane's 4 gathered bytes in the first dword) and take
+// the lane's dword out of it when a pass's math starts, where the data is
+// needed anyway.
 template <bool FULL>
-__device__ __forceinline__ u32x4 load_scales(const uint8_t* t, int SC) {
+__device__ __forceinline__ uint32_t scale_dword16(const u32x4& v, int q) {
+  if (!FULL) return v[0];
+  return q < 2 ? (q == 0 ? v[0] : v[1]) : (q == 2 ? v[2] : v[3]);
+}
+
+template <bool FULL>
+__device__ __forceinline__ void load_tile16(const uint8_t* t, int SC, u32x4 (&cq)[4], u32x4& sv) {
+  const int l = threadIdx.x & 63, r = l & 15;
+  if (FULL) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) cq[kb] = ld_weight16(t + kb * 1024 + l * 16);
+    sv = ld_weight16(t + 4096 + r * 16);
+  } else {
+    uint32_t b;
+    load_tile<false>(t, SC, cq, b);
+    sv = u32x4{b, 0u, 0u, 0u};
+  }
+}
+
+template <bool FULL>
+__device__ __forceinline__ u32x4 load_scales16(const uint8_t* t, int SC);
+
+template <bool FULL>
+__device__ __forceinline__ uint32_t load_scales(const uint8_t* t, int SC) {
   const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
-  if (FULL) return ld_weight16(t + 4096 + r * 16);
+  if (FULL) return ld_weight4(t + 4096 + r * 16 + q * 4);
   uint32_t b = 0;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) b |= (uint32_t)t[SC * 256 + r * SC + min(4 * kb + q, SC - 1)] << (8 * kb);
-  return u32x4{b, 0u, 0u, 0u};
+  for (int kb = 0; kb < 4; ++kb) b |= (uint32_t)t[SC * 256 + scale_pos(SC, r, min(4 * kb + q, SC - 1))] << (8 * kb);
+  return b;
+}
+
+template <bool FULL>
+__device__ __forceinline__ u32x4 load_scales16(const uint8_t* t, int SC) {
+  const int r = threadIdx.x & 15;
+  if (FULL) return ld_weight16(t + 4096 + r * 16);
+  return u32x4{load_scales<false>(t, SC), 0u, 0u, 0u};
 }
 
 // An address offset (always 0) that the compiler must compute after `dep`:
@@ -550,8 +591,8 @@ struct Fc1Tile {
     // issued only after the math of the pass before (its accumulator), so the
     // compiler cannot start this pass's loads early and hold a third buffer
     const uint8_t* gt = blob + 2 * tile_off(g, s, C1) + after(after(0, ag[0]), au[0]);
-    load_tile<FULL>(gt, SC, b.gq, b.gs);
-    load_tile<FULL>(gt + SC * 272, SC, b.uq, b.us);
+    load_tile16<FULL>(gt, SC, b.gq, b.gs);
+    load_tile16<FULL>(gt + SC * 272, SC, b.uq, b.us);
   }
   // x granule of step i = 4 kb + d (block 4 kb + q of the segment)
   __device__ int xg(int s, int SC, int i) const {
@@ -571,6 +612,7 @@ struct Fc1Tile {
     u32x4 xv[4], xn[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) xv[d] = xs[xg(s, SC, d)];
+    const uint32_t gsd = scale_dword16<FULL>(b.gs, q), usd = scale_dword16<FULL>(b.us, q);
     int o = 0;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -580,8 +622,8 @@ struct Fc1Tile {
       }
       const int c = 4 * kb + q;
       const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
-      const float sg = e8m0_scale(tile_scale<FULL>(b.gs, kb, q));
-      const float su = e8m0_scale(tile_scale<FULL>(b.us, kb, q));
+      const float sg = e8m0_scale(tile_scale(gsd, kb));
+      const float su = e8m0_scale(tile_scale(usd, kb));
       bf16x8 wg, wu;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -602,8 +644,8 @@ struct Fc1Tile {
       }
     }
     if (refill) {
-      b.gs = load_scales<FULL>(gt2 + o, SC2);
-      b.us = load_scales<FULL>(gt2 + SC2 * 272 + o, SC2);
+      b.gs = load_scales16<FULL>(gt2 + o, SC2);
+      b.us = load_scales16<FULL>(gt2 + SC2 * 272 + o, SC2);
     }
   }
 };
@@ -626,7 +668,7 @@ struct Fc2Tile {
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      load_tile<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s, C2) + after(after(0, acc[0][0]), acc[1][0]), SC, b.q[t], b.s[t]);
+      load_tile16<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s, C2) + after(after(0, acc[0][0]), acc[1][0]), SC, b.q[t], b.s[t]);
   }
   // h granule of step i = 4 kb + d (block 4 kb + q of the segment); odd
   // columns read the lo part
@@ -641,6 +683,7 @@ struct Fc2Tile {
     u32x4 hv[4], hn[4];  // h granules of this slab and of the next (read one slab ahead)
 #pragma unroll
     for (int d = 0; d < 4; ++d) hv[d] = hs[hg(s, SC, d)];
+    const uint32_t sd[2] = {scale_dword16<FULL>(b.s[0], q), scale_dword16<FULL>(b.s[1], q)};
     int o = 0;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -656,7 +699,7 @@ struct Fc2Tile {
         const bf16x8 h8 = __builtin_bit_cast(bf16x8, hv[d]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          wv[t] = fp4x8_bf16(b.q[t][kb][d] & msk, e8m0_scale(tile_scale<FULL>(b.s[t], kb, q)));
+          wv[t] = fp4x8_bf16(b.q[t][kb][d] & msk, e8m0_scale(tile_scale(sd[t], kb)));
           acc[t] = mfma_bf16(wv[t], h8, acc[t]);
         }
       }
@@ -672,7 +715,7 @@ struct Fc2Tile {
     }
     if (refill) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) b.s[t] = load_scales<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s + 2, C2) + o, SC2);
+      for (int t = 0; t < 2; ++t) b.s[t] = load_scales16<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s + 2, C2) + o, SC2);
     }
   }
 };
@@ -1242,7 +1285,7 @@ struct XSeg {
 //   bf16: q[m][j]  = 8 elements of row r at s*128 + 32 j + 8 q
 struct MfBuf {
   u32x4 q[2][4];
-  u32x4 s[2];
+  uint32_t s[2];
 };
 
 template <bool FP4, bool FULL>
@@ -1290,8 +1333,8 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
     for (int kb = 0; kb < 4; ++kb) {
       const int c = 4 * kb + q;
       const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
-      const float sg = e8m0_scale(tile_scale<FULL>(b.s[0], kb, q));
-      const float su = e8m0_scale(tile_scale<FULL>(b.s[1], kb, q));
+      const float sg = e8m0_scale(tile_scale(b.s[0], kb));
+      const float su = e8m0_scale(tile_scale(b.s[1], kb));
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int i = 4 * kb + d;
@@ -1524,7 +1567,7 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
       const uint32_t msk = (FULL || c < SC) ? 0xFFFFFFFFu : 0u;
       float sc[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) sc[t] = e8m0_scale(tile_scale<FULL>(b.s[t], kb, q));
+      for (int t = 0; t < 2; ++t) sc[t] = e8m0_scale(tile_scale(b.s[t], kb));
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int i = 4 * kb + d;

@@ -8,7 +8,10 @@
 // blocks 16 at a time (a "segment" s of SC = min(16, C - 16 s) blocks).  One
 // (g, s) tile holds
 //     codes  [SC][16 rows] x 16 bytes   (block 16s+c of row 16g+r at c*256 + r*16)
-//     scales [16 rows][SC] bytes
+//     scales [16 rows][SC] bytes; in a full tile (SC = 16) a row's 16 scale
+//            bytes are ordered so that its dword q holds blocks q, 4+q, 8+q,
+//            12+q (block 4 kb + q at byte 4 q + kb): the lane that decodes
+//            blocks 4 kb + q of the row loads its four scales as one dword
 // i.e. SC * 272 bytes, with every tile of a row group before the next group.
 // A wave reading tile (g, s) in 1 KB slabs gives lane l = 16 q + r the block
 // 16 s + 4 kb + q of row r in slab kb -- a contiguous 1 KB per load
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void k_pack(const uint8_t* __restrict__ src, u
     pbase = (size_t)2 * I * C1 * 17 + tile_offset(g, s, C2);
   }
   const size_t p_code = pbase + (size_t)cc * 256 + rr * 16;
-  const size_t p_scale = pbase + (size_t)SC * 256 + rr * SC + cc;
+  const size_t p_scale = pbase + (size_t)SC * 256 + (SC == 16 ? rr * 16 + (cc & 3) * 4 + (cc >> 2) : rr * SC + cc);
   const size_t row_bytes = (size_t)C * 16;
   const size_t c_code = cb.off[m] + (size_t)n * row_bytes + (size_t)c * 16;
   const size_t c_scale = cb.off[3 + m] + (size_t)n * C + c;

@@ -22,13 +22,20 @@ def canonical_parts(blob, H, I):
     return (g, gs), (u, us), (d, ds)
 
 
+# In a full tile, byte 4 q + kb of a row's 16 scale bytes holds block 4 kb + q.
+FULL_SCALE_ORDER = np.array([4 * (pos % 4) + pos // 4 for pos in range(16)])
+
+
 def tile(codes, scales, g, s):
-    """Packed tile (g, s) of one matrix: codes [SC][16 rows][16 B], then scales [16 rows][SC]."""
+    """Packed tile (g, s) of one matrix: codes [SC][16 rows][16 B], then scales [16 rows][SC]
+    (a full tile's row of 16 scale bytes in FULL_SCALE_ORDER)."""
     C = scales.shape[1]
     SC = min(16, C - 16 * s)
     rows = slice(16 * g, 16 * g + 16)
     cb = codes[rows].reshape(16, C, 16)[:, 16 * s:16 * s + SC, :]   # [row][block][16 B]
     sb = scales[rows, 16 * s:16 * s + SC]                             # [row][block]
+    if SC == 16:
+        sb = sb[:, FULL_SCALE_ORDER]
     return np.concatenate([cb.transpose(1, 0, 2).reshape(-1), sb.reshape(-1)])
 
 
@@ -72,7 +79,7 @@ def test_pack_ref_first_tile_by_hand():
     p = pack_ref(blob, H, I)
     for c, r in ((0, 0), (0, 15), (3, 7), (15, 2)):
         assert np.array_equal(p[c * 256 + r * 16:c * 256 + r * 16 + 16], g[r, 16 * c:16 * c + 16])
-        assert p[4096 + r * 16 + c] == gs[r, c]
+        assert p[4096 + r * 16 + 4 * (c % 4) + c // 4] == gs[r, c]  # block c = 4 kb + q at byte 4 q + kb
     # the up tile of (0, 0) follows the gate tile
     _, (u, us), _ = canonical_parts(blob, H, I)
     assert np.array_equal(p[4352:4352 + 16], u[0, :16])
