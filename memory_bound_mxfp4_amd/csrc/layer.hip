@@ -1219,7 +1219,7 @@ constexpr int MF_NT2 = 128 * MF_MT2;  // FC2 rows of H per unit
 constexpr int MF_XS_FP4 = 512 * 2 + 16;  // LDS column stride (bytes) of a 512-element segment
 constexpr int MF_XS_BF = 128 * 2 + 16;   // ... of a 128-element segment (bf16 weights)
 constexpr int MF_STAGE_BYTES = 2 * MF_COLS * MF_XS_FP4;  // LDS staging region of the MFMA units
-constexpr int MF_LA = 3;  // MFMA steps between an LDS read of a B fragment and its use
+constexpr int MF_LA = 2;  // MFMA steps between an LDS read of a B fragment and its use
 
 // Column list of a unit: batch rows 16 cg .. of the shared expert (a < 0),
 // or rows 16 cg .. of active expert a's row list (slot ids).
