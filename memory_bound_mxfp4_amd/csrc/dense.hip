@@ -145,13 +145,14 @@ __global__ __launch_bounds__(256) void k_dense_gemv(const uint16_t* __restrict__
   }
 }
 
-// One activation row (batch 1): a wave per weight row, two rows per wave,
-// eight per block.  Lane l takes granules l, l + 64, ... of both rows (so a
-// row's granule offsets are immediates off one base) and the matching x
-// granules once for both rows, read from global memory (the 14 KB row stays
-// in L2) -- no staging round trip and no barrier precede the weight loads.
-// Up to DG_NG granules of each row are requested before any is used.
-constexpr int DG_NG = 14;  // granules per lane, row and pass: a 7168-wide row
+// One activation row (batch 1): a wave per weight row, two waves per block
+// (3584 blocks at 7168 rows, so the stream runs on without lock-step rounds).
+// Lane l takes granules l, l + 64, ... of the row (offsets that are
+// immediates off one base) and the matching x granules, read from global
+// memory (the 14 KB row stays in L2) -- no staging round trip and no
+// barrier precede the weight loads.  Up to DG_NG granules of each are
+// requested before any is used.
+constexpr int DG_NG = 14;  // granules per lane and pass: a 7168-wide row
 
 __device__ __forceinline__ float dot_granule(const u32x4& a, const u32x4& b, float acc) {
   acc = dot2_bf16(a[0], b[0], acc);
@@ -160,42 +161,34 @@ __device__ __forceinline__ float dot_granule(const u32x4& a, const u32x4& b, flo
   return dot2_bf16(a[3], b[3], acc);
 }
 
-__global__ __launch_bounds__(256) void k_dense_gemv1(const uint16_t* __restrict__ w, int N, int K,
+__global__ __launch_bounds__(128) void k_dense_gemv1(const uint16_t* __restrict__ w, int N, int K,
                                                      const uint16_t* __restrict__ x, uint16_t* __restrict__ y) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 8 + wave * 2;
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 2 + (threadIdx.x >> 6);
   const int C8 = K / 8;
-  const uint16_t* w0 = w + (size_t)min(n0, N - 1) * K;
-  const uint16_t* w1 = w + (size_t)min(n0 + 1, N - 1) * K;
-  float a0 = 0.0f, a1 = 0.0f;
+  const uint16_t* wr = w + (size_t)min(n, N - 1) * K;
+  float acc = 0.0f;
   for (int c0 = lane; c0 < C8; c0 += 64 * DG_NG) {
-    u32x4 q0[DG_NG], q1[DG_NG], xv[DG_NG];
+    u32x4 q[DG_NG], xv[DG_NG];
     const u32x4 z{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < DG_NG; ++i) {
       const int c = c0 + 64 * i;
       const bool ok = c < C8;
-      q0[i] = ok ? ld_weight16(w0 + 8 * (size_t)c) : z;
-      q1[i] = ok ? ld_weight16(w1 + 8 * (size_t)c) : z;
+      q[i] = ok ? ld_weight16(wr + 8 * (size_t)c) : z;
       xv[i] = ok ? ld16(x + 8 * (size_t)c) : z;
     }
 #pragma unroll
-    for (int i = 0; i < DG_NG; ++i) {
-      if (c0 + 64 * i < C8) {
-        a0 = dot_granule(q0[i], xv[i], a0);
-        a1 = dot_granule(q1[i], xv[i], a1);
-      }
-    }
+    for (int i = 0; i < DG_NG; ++i)
+      if (c0 + 64 * i < C8) acc = dot_granule(q[i], xv[i], acc);
   }
-  a0 = sum_lanes<64>(a0);
-  a1 = sum_lanes<64>(a1);
-  if (lane == 0 && n0 < N) y[n0] = f32_to_bf16(a0);
-  if (lane == 0 && n0 + 1 < N) y[n0 + 1] = f32_to_bf16(a1);
+  acc = sum_lanes<64>(acc);
+  if (lane == 0 && n < N) y[n] = f32_to_bf16(acc);
 }
 
 hipError_t launch_dense_gemv(const uint16_t* w, int N, int K, const uint16_t* x, int B, uint16_t* y, hipStream_t s) {
   if (B == 1 && reinterpret_cast<uintptr_t>(x) % 16 == 0) {
-    hipLaunchKernelGGL(k_dense_gemv1, dim3((N + 7) / 8), dim3(256), 0, s, w, N, K, x, y);
+    hipLaunchKernelGGL(k_dense_gemv1, dim3((N + 1) / 2), dim3(128), 0, s, w, N, K, x, y);
     return hipGetLastError();
   }
   size_t row_bytes = (size_t)K * 2;
