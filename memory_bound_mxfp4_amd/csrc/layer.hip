@@ -897,6 +897,16 @@ __device__ __forceinline__ void router_unit(const LayerParams& p, WgState& st, i
 // last value) replace 6 per value.  Lane l ends with the total of value
 // (l >> (6 - log2 N)) ... for N 32: value (l >> 1) & 31, held by lanes 2 m and
 // 2 m + 1.
+// The thread index through an empty asm, for the batch > 1 units: values
+// derived from it cannot be hoisted out of the unit loop, where they would
+// hold registers across every other unit (the batch > 1 kernel is register
+// bound); each unit recomputes them.
+__device__ __forceinline__ int tidx() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 template <int CNT, int M, int N>
 __device__ __forceinline__ void reduce_scatter_step(double (&v)[N], int lane) {
   if constexpr (CNT > 1) {
@@ -932,7 +942,7 @@ __device__ __forceinline__ double reduce_scatter_f64(double (&v)[N]) {
 __device__ __forceinline__ void router_mf_unit(const LayerParams& p, WgState& st, Lds& L, int u) {
   constexpr int RB = 8, EW = 4;  // rows and experts per unit
   const int eg = u % p.n_rt_e, rb = u / p.n_rt_e;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = tidx() >> 6, lane = tidx() & 63;
   const int e0 = EW * eg, b0 = RB * rb, nr = min(RB, p.B - b0);
   const int C = p.H / 8, Q = (C + 3) / 4, c_lo = w * Q, c_hi = min(C, c_lo + Q);
   const int J = (Q + 63) / 64;
@@ -974,8 +984,8 @@ __device__ __forceinline__ void router_mf_unit(const LayerParams& p, WgState& st
   __syncthreads();  // L.red is free (the previous unit is done with it)
   if ((lane & 1) == 0) part[w * 32 + (lane >> 1)] = v;
   __syncthreads();
-  if (threadIdx.x < EW * RB) {
-    const int i = threadIdx.x, e = e0 + i / RB, r = i % RB;
+  if (tidx() < EW * RB) {
+    const int i = tidx(), e = e0 + i / RB, r = i % RB;
     if (e < p.E && r < nr) {
       const double bb = p.bias ? (double)p.bias[e] : 0.0;
       const double t = ((part[i] + part[32 + i]) + part[64 + i]) + part[96 + i];
@@ -1290,7 +1300,7 @@ struct MfBuf {
 
 template <bool FP4, bool FULL>
 __device__ __forceinline__ void mf1_load(const LayerParams& p, const uint8_t* blob, int g, int s, MfBuf& b, float dep) {
-  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int lane = tidx() & 63, r = lane & 15, q = lane >> 4;
   if (FP4) {
     const int C1 = p.H / 32;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
@@ -1314,7 +1324,7 @@ __device__ __forceinline__ void mf1_load(const LayerParams& p, const uint8_t* bl
 template <bool FP4, bool FULL>
 __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBuf& b, const char* xb, int xoff,
                                          bool live, f32x4& ag, f32x4& au) {
-  const int lane = threadIdx.x & 63, q = lane >> 4;
+  const int lane = tidx() & 63, q = lane >> 4;
   const u32x4 z{0u, 0u, 0u, 0u};
   if (FP4) {
     const int C1 = p.H / 32;
@@ -1363,7 +1373,7 @@ __device__ __forceinline__ void mf_fc1_unit(const LayerParams& p, WgState& st, L
   constexpr int KS = FP4 ? 512 : 128, XS = KS * 2 + 16;
   load_cols(p, st, L, a, cg);
   const int nc = L.nrows;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
   const int N = FP4 ? p.I : p.Is;
   const int g = 4 * t + w;
   const uint8_t* blob = FP4 ? p.experts + (size_t)st.s_active[a] * p.blob_bytes : nullptr;
@@ -1379,7 +1389,7 @@ __device__ __forceinline__ void mf_fc1_unit(const LayerParams& p, WgState& st, L
     // the weights stream with no barrier (the common case at small batch).
     constexpr int PER = 8;
     const int CPC = p.H / 8, total = nc * CPC;
-    for (int base = threadIdx.x; base < total; base += 256 * PER) {
+    for (int base = tidx(); base < total; base += 256 * PER) {
       u32x4 v[PER];
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
@@ -1440,7 +1450,7 @@ __device__ __forceinline__ void mf_fc1_unit(const LayerParams& p, WgState& st, L
   }
   __builtin_amdgcn_s_waitcnt(0);  // every lane's h stores have completed
   __syncthreads();
-  if (threadIdx.x == 0) st_coh(hflag_at(p, a < 0 ? p.umax : a, cg, t), make_pair(1u, st.tag));
+  if (tidx() == 0) st_coh(hflag_at(p, a < 0 ? p.umax : a, cg, t), make_pair(1u, st.tag));
 }
 
 // Shared-expert FC1 + SwiGLU at batch > 1 (bf16 weights): one 16-row group g
@@ -1455,7 +1465,7 @@ template <bool FULL>
 __device__ __forceinline__ void mf_sh1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int cg, int g) {
   load_cols(p, st, L, -1, cg);
   const int nc = L.nrows;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
   const int S = (p.H + 127) / 128;
   const int P = w < S ? (S - w + 3) / 4 : 0;
   const bool live = r < nc;
@@ -1499,7 +1509,7 @@ __device__ __forceinline__ void mf_sh1_unit(const LayerParams& p, WgState& st, L
   }
   __syncthreads();
   {
-    const int row = threadIdx.x >> 4, col = threadIdx.x & 15, n = 16 * g + row;
+    const int row = tidx() >> 4, col = tidx() & 15, n = 16 * g + row;
     float vg = 0.f, vu = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
@@ -1511,7 +1521,7 @@ __device__ __forceinline__ void mf_sh1_unit(const LayerParams& p, WgState& st, L
   }
   __builtin_amdgcn_s_waitcnt(0);  // every thread's h stores have completed
   __syncthreads();
-  if (threadIdx.x == 0) st_coh(hflag_at(p, p.umax, cg, g), make_pair(1u, st.tag));
+  if (tidx() == 0) st_coh(hflag_at(p, p.umax, cg, g), make_pair(1u, st.tag));
 }
 
 // One FC2 segment of a wave: two 16-row A tiles of the down matrix.
@@ -1520,7 +1530,7 @@ __device__ __forceinline__ void mf_sh1_unit(const LayerParams& p, WgState& st, L
 template <bool FP4, bool FULL>
 __device__ __forceinline__ void mf2_load(const LayerParams& p, const uint8_t* down, const int (&gt)[2], int s,
                                          MfBuf& b, float dep) {
-  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int lane = tidx() & 63, r = lane & 15, q = lane >> 4;
   if (FP4) {
     const int C2 = p.I / 32;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
@@ -1545,7 +1555,7 @@ __device__ __forceinline__ void mf2_load(const LayerParams& p, const uint8_t* do
 template <bool FP4, bool FULL>
 __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBuf& b, const char* hb, const char* lob,
                                          int hoff, bool live, f32x4 (&acc)[2]) {
-  const int lane = threadIdx.x & 63, q = lane >> 4;
+  const int lane = tidx() & 63, q = lane >> 4;
   const u32x4 z{0u, 0u, 0u, 0u};
   if (FP4) {
     const int C2 = p.I / 32;
@@ -1612,7 +1622,7 @@ template <int PER>
 __device__ __forceinline__ void mf_stage_h(const LayerParams& p, const Lds& L, const float* hsrc, int K, int k0,
                                            int KE, int nc, int ncols, char* hb, int XS, int lo_off) {
   const int HP = KE / 2, total = ncols * HP;  // element pairs
-  for (int base = threadIdx.x; base < total; base += 256 * PER) {
+  for (int base = tidx(); base < total; base += 256 * PER) {
     uint64_t v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -1653,7 +1663,7 @@ template <bool FP4, bool FULL>
 __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
   load_cols(p, st, L, a, cg);
   const int nc = L.nrows;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
   const int K = FP4 ? p.I : p.Is;
   const int G = p.H / 16;
   const uint8_t* down =
@@ -1696,9 +1706,9 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
   {  // wait until every FC1 tile (shared expert: 16-row group) of this column group has published its h
     const int ntile = FP4 ? (K + MF_NT1 - 1) / MF_NT1 : (K + 15) / 16;
     bool ok = true;
-    if ((int)threadIdx.x < ntile) {
+    if (tidx() < ntile) {
       uint64_t f[1];
-      const int ti = threadIdx.x;
+      const int ti = tidx();
       ok = poll_pairs<1>(hflag_at(p, a < 0 ? p.umax : a, cg, 0), 1, [&](int) { return ti; }, st.tag, f, SPIN_LIMIT,
                          p.ctrl + CTRL_ERR);
     }
