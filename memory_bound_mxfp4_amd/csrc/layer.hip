@@ -51,6 +51,17 @@
 
 namespace moe {
 
+// The thread index through an empty asm, for the batch > 1 code: values
+// derived from it cannot be hoisted out of the unit loop, where they would
+// hold registers across every other unit (the batch > 1 kernel is register
+// bound); each unit recomputes them.
+__device__ __forceinline__ int tidx() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+
 constexpr int NT1 = 16;   // routed FC1 rows (of I) per unit: one packed row group, 16 x 2 x 3.8 KB at H 7168
 constexpr int NTS1 = 4;   // shared FC1 rows (of Is) per unit: 4 x 2 x 14 KB of bf16
 constexpr int NT2 = 256;  // combine tile (rows of H)
@@ -160,30 +171,32 @@ __device__ __forceinline__ uint32_t poll_ready(const LayerParams& p, uint32_t ta
 // "active expert" j with row list {j}; its expert comes from the routing
 // pairs.  Batch > 1: wait for the schedule unit's ready word, then copy the
 // published schedule (one batch of coherent loads).
+template <bool OPQ>
 __device__ __forceinline__ void cache_schedule(const LayerParams& p, WgState& st, Lds& L, int* sc) {
+  const int TID_ = OPQ ? tidx() : (int)threadIdx.x;
   int* a = sc;
   int* ro = sc + p.umax;
   int* rw = ro + p.umax + 1;
   int* cgo = rw + p.B * p.k;
   if (p.B == 1) {
-    if (threadIdx.x < p.k) {
+    if (TID_ < p.k) {
       uint64_t v[1];
-      const int j = threadIdx.x;
+      const int j = TID_;
       if (!poll_pairs<1>(p.idx_p, 1, [&](int) { return j; }, st.tag, v, SPIN_LIMIT, p.ctrl + CTRL_ERR)) set_error(p);
       a[j] = (int)min((uint32_t)v[0], (uint32_t)p.E - 1u);
       ro[j] = j;
       rw[j] = j;
     }
-    if (threadIdx.x == 0) {
+    if (TID_ == 0) {
       ro[p.k] = p.k;
       L.U = p.k;
     }
   } else {
-    if (threadIdx.x == 0) L.U = (int)min(poll_ready(p, st.tag), (uint32_t)p.umax);
+    if (TID_ == 0) L.U = (int)min(poll_ready(p, st.tag), (uint32_t)p.umax);
     __syncthreads();
     const int U = L.U, nslots = p.B * p.k;
     const int total = U + (U + 1) + nslots + (U + 1);
-    for (int base = threadIdx.x; base < total; base += 256 * 8) {
+    for (int base = TID_; base < total; base += 256 * 8) {
       int v[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -466,9 +479,10 @@ __device__ __forceinline__ uint32_t ld_weight4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
-template <bool FULL>
+// OPQ: take the thread index through tidx() (the batch > 1 units).
+template <bool FULL, bool OPQ = false>
 __device__ __forceinline__ void load_tile(const uint8_t* t, int SC, u32x4 (&cq)[4], uint32_t& sv) {
-  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  const int l = (OPQ ? tidx() : (int)threadIdx.x) & 63, r = l & 15, q = l >> 4;
   if (FULL) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) cq[kb] = ld_weight16(t + kb * 1024 + l * 16);
@@ -766,10 +780,12 @@ __device__ __forceinline__ void stage_h_split(const LayerParams& p, const WgStat
 
 // Expert-gathered schedule from the routing pairs of all B*k slots (LDS
 // counting; 256 threads).  LDS: cnt[E], start[E], ids[B*k].
+template <bool OPQ>
 __device__ __forceinline__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt, int* wtot /* LDS [8] */) {
+  const int TID_ = OPQ ? tidx() : (int)threadIdx.x;
   int* start = cnt + p.E;
   int* ids = start + p.E;
-  const int t = threadIdx.x, nslots = p.B * p.k;
+  const int t = TID_, nslots = p.B * p.k;
   bool ok = true;
   for (int base = t; base < nslots; base += 256 * 8) {
     uint64_t v[8];
@@ -897,15 +913,6 @@ __device__ __forceinline__ void router_unit(const LayerParams& p, WgState& st, i
 // last value) replace 6 per value.  Lane l ends with the total of value
 // (l >> (6 - log2 N)) ... for N 32: value (l >> 1) & 31, held by lanes 2 m and
 // 2 m + 1.
-// The thread index through an empty asm, for the batch > 1 units: values
-// derived from it cannot be hoisted out of the unit loop, where they would
-// hold registers across every other unit (the batch > 1 kernel is register
-// bound); each unit recomputes them.
-__device__ __forceinline__ int tidx() {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
-}
 
 template <int CNT, int M, int N>
 __device__ __forceinline__ void reduce_scatter_step(double (&v)[N], int lane) {
@@ -1169,17 +1176,19 @@ __device__ __forceinline__ void routed_fc2_unit(const LayerParams& p, WgState& s
 // Combine unit (row b, tile t of NT2 rows of H): residual += shared output +
 // sum_j gate_j * o_j in fixed j order, polling the outputs until they are
 // this call's.  Thread i owns row m = t*NT2 + i.
+template <bool OPQ>
 __device__ __forceinline__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, int t) {
+  const int TID_ = OPQ ? tidx() : (int)threadIdx.x;
   __syncthreads();
   const size_t s0 = (size_t)b * p.k;
-  if (threadIdx.x < p.k) {
+  if (TID_ < p.k) {
     uint64_t g[1];
-    if (!poll_pairs<1>(p.gate_p + s0, 1, [&](int) { return (int)threadIdx.x; }, st.tag, g, SPIN_LIMIT, p.ctrl + CTRL_ERR))
+    if (!poll_pairs<1>(p.gate_p + s0, 1, [&](int) { return TID_; }, st.tag, g, SPIN_LIMIT, p.ctrl + CTRL_ERR))
       set_error(p);
-    L.gates[threadIdx.x] = pair_f32(g[0]);
+    L.gates[TID_] = pair_f32(g[0]);
   }
   __syncthreads();
-  const int m = t * NT2 + threadIdx.x;
+  const int m = t * NT2 + TID_;
   if (m >= p.H) return;
   float acc = p.residual[(size_t)b * p.H + m];
   bool ok = true;
@@ -1305,8 +1314,8 @@ __device__ __forceinline__ void mf1_load(const LayerParams& p, const uint8_t* bl
     const int C1 = p.H / 32;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
     const uint8_t* gt = blob + 2 * tile_off(g, s, C1) + after(0, dep);
-    load_tile<FULL>(gt, SC, b.q[0], b.s[0]);
-    load_tile<FULL>(gt + SC * 272, SC, b.q[1], b.s[1]);
+    load_tile<FULL, true>(gt, SC, b.q[0], b.s[0]);
+    load_tile<FULL, true>(gt + SC * 272, SC, b.q[1], b.s[1]);
   } else {
     const int n = min(16 * g + r, p.Is - 1);
 #pragma unroll
@@ -1535,7 +1544,7 @@ __device__ __forceinline__ void mf2_load(const LayerParams& p, const uint8_t* do
     const int C2 = p.I / 32;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) load_tile<FULL>(down + tile_off(gt[t], s, C2) + after(0, dep), SC, b.q[t], b.s[t]);
+    for (int t = 0; t < 2; ++t) load_tile<FULL, true>(down + tile_off(gt[t], s, C2) + after(0, dep), SC, b.q[t], b.s[t]);
   } else {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -1826,7 +1835,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
       routing_unit<TPL>(p, st, L, reinterpret_cast<int*>(xs), rel);
     } else if ((rel -= p.n_ro) < p.n_sch) {
       __syncthreads();
-      build_schedule(p, st, reinterpret_cast<int*>(xs), L.wtot);
+      build_schedule<MF>(p, st, reinterpret_cast<int*>(xs), L.wtot);
       st.x_cached = false;
     } else if ((rel -= p.n_sch) < p.n_s1) {
       if constexpr (MF) mf_sh1_unit<FULL>(p, st, L, mfb, rel / p.mf_t1s, rel % p.mf_t1s);
@@ -1835,7 +1844,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
       rel -= p.n_s1;
       if (!st.route_seen) {
         __syncthreads();
-        cache_schedule(p, st, L, sched_lds);
+        cache_schedule<MF>(p, st, L, sched_lds);
       }
       const int U = st.U;
       if constexpr (MF) {
@@ -1849,7 +1858,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
           const int gc = rel / p.mf_t2, ae = find_expert(st, gc);
           mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, gc - st.s_cg_off[ae], rel % p.mf_t2);
         } else if ((rel -= NCG * p.mf_t2) < p.B * p.n_tile) {
-          combine_unit(p, st, L, rel / p.n_tile, rel % p.n_tile);
+          combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile);
         } else {
           break;
         }
@@ -1861,7 +1870,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
         } else if ((rel -= p.n_s2) < U * p.n_r2) {
           routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / p.n_r2, rel % p.n_r2);
         } else if ((rel -= U * p.n_r2) < p.B * p.n_tile) {
-          combine_unit(p, st, L, rel / p.n_tile, rel % p.n_tile);
+          combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile);
         } else {
           break;
         }
