@@ -876,7 +876,7 @@ __device__ __forceinline__ void build_schedule(const LayerParams& p, const WgSta
 __device__ __forceinline__ void router_unit(const LayerParams& p, WgState& st, int u) {
   constexpr int NG = 14;  // granules in flight per lane: a whole row at H 7168
   const int lane = threadIdx.x & 63;
-  const int e = 4 * u + (threadIdx.x >> 6);
+  const int e = 4 * u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int C = p.H / 8;
   const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wr + (size_t)min(e, p.E - 1) * p.H);
   const u32x4* xr = reinterpret_cast<const u32x4*>(p.x);
@@ -1063,9 +1063,9 @@ __device__ __forceinline__ void shared_fc1_unit(const LayerParams& p, WgState& s
 template <int RG, bool FULL>
 __device__ __forceinline__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g) {
   // batch 1: active expert a has exactly one row, its slot (no LDS row list, no barrier)
-  const int slot = st.s_rows[st.s_row_off[a]];
-  const uint8_t* blob = p.experts + (size_t)st.s_active[a] * p.blob_bytes;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[a]]);
+  const uint8_t* blob = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[a]) * p.blob_bytes;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // w: wave-uniform (scalar)
   const int C1 = p.H / 32, S1 = (C1 + 15) / 16;
   const int P = w < S1 ? (S1 - w + 3) / 4 : 0;
   {
@@ -1138,10 +1138,11 @@ __device__ __forceinline__ void shared_fc2_unit(const LayerParams& p, WgState& s
 // takes groups 8v + w and 8v + w + 4 and runs one pass per segment along I.
 template <int RG, bool FULL>
 __device__ __forceinline__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v) {
-  const int slot = st.s_rows[st.s_row_off[a]];  // batch 1: the active expert's one row
+  const int slot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[a]]);  // batch 1: the active expert's one row
   const int C1 = p.H / 32, C2 = p.I / 32, S2 = (C2 + 15) / 16;
-  const uint8_t* down = p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * C1 * 17;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint8_t* down = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[a]) * p.blob_bytes +
+                        (size_t)2 * p.I * C1 * 17;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // w: wave-uniform (scalar)
   const int G = p.H / 16, g0 = 8 * v + w;
   const int ng = g0 < G ? (g0 + 4 < G ? 2 : 1) : 0;
   const int P = ng > 0 ? S2 : 0;
@@ -1821,7 +1822,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   if (u < 0) {
     if (threadIdx.x == 0) L.next = p.n_static + (int)__hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    u = L.next;
+    u = __builtin_amdgcn_readfirstlane(L.next);
   }
   int it = 0;
   for (;;) {
@@ -1881,7 +1882,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     // cannot overwrite one that a slower wave has yet to read.
     if (threadIdx.x == 0) L.nxt[it & 1] = p.n_static + (int)nxt;
     __syncthreads();
-    u = L.nxt[it & 1];
+    u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);  // uniform: unit arithmetic stays scalar
     ++it;
   }
   // Exit: the last workgroup out resets the queue and advances the epoch (all
