@@ -151,6 +151,24 @@ def test_k3_batch64_zipf(k3_layer):
     _check(cfg, 0, x, res, out, idx, gate, rows=[0, 31, 63])
 
 
+@pytest.mark.parametrize("B", [4, 16, 33])
+def test_k3_verify_and_ragged_batches(k3_layer, B):
+    """Verify-step batch shapes (4 and 16 rows) and a ragged one (33 rows: a
+    partial router row block and a one-row column group): every row's
+    indices and gates against the oracle, outputs on the first and last row."""
+    cfg = CONFIGS["k3_b8"]
+    print(f"[case] layer K3 B{B} seed 0", flush=True)
+    x = x_host(cfg, 0, variant=5, batch=B)
+    res = residual_from_x(x)
+    out, idx, gate = _run_layer(k3_layer, x, res)
+    hw = host_weights(cfg, 0)
+    lg, _ = oracle.router_logits(x, hw["router_w"], hw["router_bias"], cfg.hidden, cfg.num_experts)
+    idx_ref, gate_ref = oracle.topk(lg, cfg.top_k)
+    assert np.array_equal(idx, idx_ref)
+    assert np.abs(gate - gate_ref).max() <= 1e-6
+    _check(cfg, 0, x, res, out, idx, gate, rows=[0, B - 1])
+
+
 def test_k3_deterministic(k3_layer):
     import torch
     cfg = CONFIGS["k3_b8"]
