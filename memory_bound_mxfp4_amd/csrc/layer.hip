@@ -1241,19 +1241,21 @@ constexpr int MF_XS_BF = 128 * 2 + 16;   // ... of a 128-element segment (bf16 w
 constexpr int MF_STAGE_BYTES = 2 * MF_COLS * MF_XS_FP4;  // LDS staging region of the MFMA units
 constexpr int MF_LA = 2;  // MFMA steps between an LDS read of a B fragment and its use
 
+// Number of columns of a unit's column group, from this workgroup's copy of
+// the schedule (no barrier): what load_cols publishes as L.nrows.
+__device__ __forceinline__ int unit_ncols(const LayerParams& p, const WgState& st, int a, int cg) {
+  if (a < 0) return min(MF_COLS, p.B - MF_COLS * cg);
+  return min(MF_COLS, st.s_row_off[a + 1] - (st.s_row_off[a] + MF_COLS * cg));
+}
+
 // Column list of a unit: batch rows 16 cg .. of the shared expert (a < 0),
 // or rows 16 cg .. of active expert a's row list (slot ids).
 __device__ __forceinline__ void load_cols(const LayerParams& p, const WgState& st, Lds& L, int a, int cg) {
   __syncthreads();
-  if (a < 0) {
-    const int n = min(MF_COLS, p.B - MF_COLS * cg);
-    if ((int)threadIdx.x < n) L.slot[threadIdx.x] = MF_COLS * cg + threadIdx.x;
-    if (threadIdx.x == 0) L.nrows = n;
-  } else {
-    const int r0 = st.s_row_off[a] + MF_COLS * cg, n = min(MF_COLS, st.s_row_off[a + 1] - r0);
-    if ((int)threadIdx.x < n) L.slot[threadIdx.x] = st.s_rows[r0 + threadIdx.x];
-    if (threadIdx.x == 0) L.nrows = n;
-  }
+  const int n = unit_ncols(p, st, a, cg);
+  if ((int)threadIdx.x < n) L.slot[threadIdx.x] = a < 0 ? MF_COLS * cg + threadIdx.x
+                                                         : st.s_rows[st.s_row_off[a] + MF_COLS * cg + threadIdx.x];
+  if (threadIdx.x == 0) L.nrows = n;
   __syncthreads();
 }
 
@@ -1381,8 +1383,6 @@ __device__ __forceinline__ void mf1_math(const LayerParams& p, int s, const MfBu
 template <bool FP4, bool FULL>
 __device__ __forceinline__ void mf_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
   constexpr int KS = FP4 ? 512 : 128, XS = KS * 2 + 16;
-  load_cols(p, st, L, a, cg);
-  const int nc = L.nrows;
   const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
   const int N = FP4 ? p.I : p.Is;
   const int g = 4 * t + w;
@@ -1393,6 +1393,8 @@ __device__ __forceinline__ void mf_fc1_unit(const LayerParams& p, WgState& st, L
   MfBuf ba, bb;
   mf1_load<FP4, FULL>(p, blob, gl, 0, ba, 0.f);
   if (S > 1) mf1_load<FP4, FULL>(p, blob, gl, 1, bb, 0.f);
+  load_cols(p, st, L, a, cg);  // after the first weight loads: its barriers overlap them
+  const int nc = L.nrows;
   const int XF = p.H * 2 + 16;  // column stride of whole-K staging
   if (nc * XF <= MF_STAGE_BYTES) {
     // Narrow column group: all of K for every column in LDS at once, then
@@ -1671,8 +1673,7 @@ __device__ __forceinline__ void mf_stage_h(const LayerParams& p, const Lds& L, c
 // stages h 512 elements at a time.
 template <bool FP4, bool FULL>
 __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg, int t) {
-  load_cols(p, st, L, a, cg);
-  const int nc = L.nrows;
+  const int nc = unit_ncols(p, st, a, cg);
   const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
   const int K = FP4 ? p.I : p.Is;
   const int G = p.H / 16;
@@ -1713,6 +1714,7 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
       mf2_load<FP4, FULL>(p, down, gt, by_tile ? 0 : 1 % S, bb, 0.f);
     }
   }
+  load_cols(p, st, L, a, cg);  // after the first weight loads: its barriers overlap them
   {  // wait until every FC1 tile (shared expert: 16-row group) of this column group has published its h
     const int ntile = FP4 ? (K + MF_NT1 - 1) / MF_NT1 : (K + 15) / 16;
     bool ok = true;
