@@ -781,7 +781,7 @@ __device__ __forceinline__ void stage_h_split(const LayerParams& p, const WgStat
 // Expert-gathered schedule from the routing pairs of all B*k slots (LDS
 // counting; 256 threads).  LDS: cnt[E], start[E], ids[B*k].
 template <bool OPQ>
-__device__ __forceinline__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt, int* wtot /* LDS [8] */) {
+__device__ __forceinline__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt, int* wtot /* LDS [12] */) {
   const int TID_ = OPQ ? tidx() : (int)threadIdx.x;
   int* start = cnt + p.E;
   int* ids = start + p.E;
@@ -1624,8 +1624,6 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
   }
 }
 
-// h segment [s*KS, s*KS + KS) of the unit's columns (fp32, written by this
-// launch's FC1 units: 8-byte coherent loads) into LDS as bf16 hi and lo.
 // Columns [0, ncols) x elements [k0, k0 + KE) of h (fp32, written by this
 // launch's FC1 units: 8-byte coherent loads, PER per thread per batch) into
 // LDS as bf16 hi halves (column c at hb + c * XS) and lo halves (at
