@@ -298,7 +298,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the layer fits one MI355X; "
-              "this build has no multi-GPU path)", file=sys.stderr)
+              "there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch
