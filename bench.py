@@ -16,10 +16,11 @@ from each step's actual routing) + activations.
 
 Prints ONE JSON line.  `value` is algorithmic bytes over the wall time of K
 steps launched back to back.  `roofline` is for the dominant kernel -- the
-layer is a single persistent kernel, k_moe_layer -- timed in a second pass
-over the same steps with HIP events recorded by the library around each
-launch on the launch stream; `cpu_baseline` is the CPU oracle on one batch-1
-layer (single thread).
+layer is a single persistent kernel, k_moe_layer -- whose average launch
+duration is the span of two HIP events recorded on the launch stream around
+those K launches, divided by K.  Every timed step is then re-run alone and
+must reproduce its residual bit for bit (`validated`).  `cpu_baseline` is the
+CPU oracle on one batch-1 layer, on all host threads and on one.
 """
 from __future__ import annotations
 
@@ -54,13 +55,42 @@ def layer_bytes(cfg, idx, with_bias: bool):
     return {"total": total, "U": U, "per_kernel": per_kernel}
 
 
-def run_config(cfg, layers, steps, warmup, variants, seed=0):
-    """Times `steps` layer steps. Returns a dict of measurements."""
+def _step_args(lib, w, x, res, idx, gate, ws, stream):
+    """The ctypes argument tuple of one moe_decode_layer call (built outside the
+    timed loop, so the loop costs one foreign call per step)."""
+    import ctypes
+    import memory_bound_mxfp4_amd as moe
+    cs = w.c_struct()
+    return (ctypes.byref(cs), moe._ptr(x), moe._ptr(res), x.shape[0], moe._ptr(idx), moe._ptr(gate), moe._ptr(ws),
+            ws.numel(), moe._stream(stream)), cs
+
+
+def _pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v, np.float64), q))
+
+
+def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None):
+    """Times `steps` layer steps launched back to back, then checks them.
+
+    * timed pass: K steps enqueued back to back (one foreign call each);
+      wall clock between two synchronisations, and two HIP events recorded on
+      the launch stream before the first and after the last launch (the GPU
+      span, which the host's launch rate cannot stretch once the queue is
+      ahead of the GPU);
+    * validation: the workspace status word must read 0, and every timed
+      step's residual and indices must be bit-identical to the same step
+      re-run alone (synchronised) on the same inputs -- a launch that
+      overlapped its predecessor or took stale data would differ;
+    * per-launch events: `event_reps` more launches, each bracketed by events
+      recorded by the library, for the median / p10 / p90 of one launch.
+    """
     import numpy as np
     import torch
 
     import memory_bound_mxfp4_amd as moe
     from layer_inputs import residual_from_x, x_host
+    lib = moe.load()
     B = cfg.batch
     names = moe.layer_kernel_names()
     xs = [torch.from_numpy(x_host(cfg, seed, variant=v)).cuda() for v in range(variants)]
@@ -77,50 +107,74 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0):
     saved_bias = [w.router_bias for w in layers]
     for w in layers:
         w.router_bias = bias
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     stream = torch.cuda.current_stream()
-    res_t = [res0[s % variants].clone() for s in range(steps)]  # residuals of the per-kernel-event pass
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    event_reps = steps if event_reps is None else event_reps
     try:
+        args, keep = [], []
+        for s in range(total):
+            a, cs = _step_args(lib, layers[s % len(layers)], xs[s % variants], res[s], idx[s], gate[s], ws, stream)
+            args.append(a)
+            keep.append(cs)
+        call = lib.moe_decode_layer
         for s in range(warmup):
-            w = layers[s % len(layers)]
-            moe.moe_decode_layer(w, xs[s % variants], res[s], idx=idx[s], gate=gate[s], ws=ws)
+            assert call(*args[s]) == moe.MOE_OK
         torch.cuda.synchronize()
         # Timed pass: K steps launched back to back (the throughput `value`).
         t0 = time.perf_counter()
-        for i in range(steps):
-            s = warmup + i
-            w = layers[s % len(layers)]
-            moe.moe_decode_layer(w, xs[s % variants], res[s], idx=idx[s], gate=gate[s], ws=ws, stream=stream)
+        e0.record(stream)
+        for s in range(warmup, total):
+            call(*args[s])
+        e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        # Second pass over the same steps with HIP events recorded by the
-        # library around each kernel on the launch stream (the roofline's
-        # average launch duration).
+        status = moe.workspace_status(ws)
+        # Validation: each timed step again, alone, from the same inputs.
+        mismatches = 0
         for i in range(steps):
             s = warmup + i
-            w = layers[s % len(layers)]
-            moe.moe_decode_layer_timed(w, xs[s % variants], res_t[i], idx[s], gate[s], ws, events[i], stream=stream)
+            r_v = res0[s % variants].clone()
+            i_v = torch.empty_like(idx[s])
+            g_v = torch.empty_like(gate[s])
+            moe.moe_decode_layer(layers[s % len(layers)], xs[s % variants], r_v, idx=i_v, gate=g_v, ws=ws)
+            torch.cuda.synchronize()
+            same = torch.equal(r_v.view(torch.int32), res[s].view(torch.int32)) and torch.equal(i_v, idx[s])
+            mismatches += 0 if same else 1
+        status = status | moe.workspace_status(ws)
+        # Per-launch events (the library records them around its kernel).
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(event_reps)]
+        for i in range(event_reps):
+            s = warmup + i % steps
+            r_e = res0[s % variants].clone()
+            moe.moe_decode_layer_timed(layers[s % len(layers)], xs[s % variants], r_e, idx[s], gate[s], ws, ev[i],
+                                       stream=stream)
         torch.cuda.synchronize()
     finally:
         for w, b in zip(layers, saved_bias):
             w.router_bias = b
     wall_s = t1 - t0
+    span_ms = e0.elapsed_time(e1)
     idx_h = idx[warmup:].cpu().numpy()
     per = [layer_bytes(cfg, idx_h[i], bias is not None) for i in range(steps)]
     tot_bytes = sum(p["total"] for p in per)
-    kern_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)]))
-               for j, n in enumerate(names)}
-    gpu_span_ms = events[0][0].elapsed_time(events[-1][-1])
+    launch_us = {n: [ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(event_reps)]
+                 for j, n in enumerate(names)}
     kb = {n: float(np.mean([p["per_kernel"][n] for p in per])) for n in per[0]["per_kernel"]}
     return {
         "wall_s": wall_s,
         "us_per_layer": wall_s / steps * 1e6,
-        "gpu_us_per_layer": gpu_span_ms / steps * 1e3,
+        "gpu_span_us_per_layer": span_ms / steps * 1e3,
         "gbps": tot_bytes / wall_s / 1e9,
+        "gbps_gpu_span": tot_bytes / (span_ms * 1e-3) / 1e9,
         "bytes_per_layer": tot_bytes / steps,
         "U_mean": float(np.mean([p["U"] for p in per])),
-        "kernel_us": {n: v * 1e3 for n, v in kern_ms.items()},
+        "U_min": int(min(p["U"] for p in per)),
+        "U_max": int(max(p["U"] for p in per)),
         "kernel_bytes": kb,
+        "launch_us": {n: {"median": round(_pct(v, 50), 2), "p10": round(_pct(v, 10), 2), "p90": round(_pct(v, 90), 2),
+                          "reps": len(v)} for n, v in launch_us.items()},
+        "validated": {"status_word": int(status), "steps_bit_identical_to_serial_rerun": steps - mismatches,
+                      "steps": steps, "ok": status == 0 and mismatches == 0},
     }
 
 
@@ -200,9 +254,20 @@ def pmc_summary(fetch_csv, write_csv, kernel="k_moe_layer"):
             "kernel_source_hash": kernel_source_hash()}
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seed=0):
-    """The oracle (single thread) on one K3-shaped batch-1 layer; expert regeneration excluded."""
-    import numpy as np
+    """The oracle on one K3-shaped batch-1 layer, once on one thread and once
+    on every host thread (its expert evaluations spread by OpenMP); expert
+    regeneration excluded.  About 7 s of CPU time on this class of host."""
     import oracle
     from layer_inputs import host_experts, host_weights, residual_from_x, x_host
     from synth import CONFIGS
@@ -213,15 +278,94 @@ def cpu_baseline(seed=0):
     lg, _ = oracle.router_logits(x, hw["router_w"], None, cfg.hidden, cfg.num_experts)
     idx, _ = oracle.topk(lg, cfg.top_k)
     experts = host_experts(cfg, seed, idx.ravel())
-    t0 = time.perf_counter()
-    r = oracle.moe_layer(cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.shared_inter, hw["router_w"], None,
-                         hw["shared_gate"], hw["shared_up"], hw["shared_down"], experts, x, res)
-    dt = time.perf_counter() - t0
+    nproc = os.cpu_count() or 1
+    n_all = oracle.set_threads(0)
+    times = {}
+    try:
+        for n in (1, n_all):
+            oracle.set_threads(n)
+            t0 = time.perf_counter()
+            r = oracle.moe_layer(cfg.hidden, cfg.inter, cfg.num_experts, cfg.top_k, cfg.shared_inter, hw["router_w"],
+                                 None, hw["shared_gate"], hw["shared_up"], hw["shared_down"], experts, x, res)
+            times[n] = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(n_all)
     nbytes = layer_bytes(cfg, r["idx"], False)["total"]
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_layer": round(dt * 1e6, 1),
-            "sample": "one K3-shaped batch-1 layer (hidden 7168, 896 experts, top-16, seed 0), router + top-k + "
-                      "shared + 16 routed experts + combine, single thread; expert regeneration excluded"}
+    return {"value": round(nbytes / times[n_all] / 1e9, 4), "unit": "GB/s", "cores": n_all, "kind": "oracle",
+            "us_per_layer": round(times[n_all] * 1e6, 1),
+            "single_thread": {"value": round(nbytes / times[1] / 1e9, 4), "us_per_layer": round(times[1] * 1e6, 1)},
+            "host": {"nproc": nproc, "cpu_model": _cpu_model(), "omp_threads": n_all},
+            "sample": "one K3-shaped batch-1 layer (hidden 7168, 896 experts, top-16, seed 0): router + top-k + "
+                      "shared + 16 routed experts + combine; value on `cores` threads (17 independent expert "
+                      "evaluations spread by OpenMP), single_thread on one; expert regeneration excluded"}
+
+
+def stream_ceiling(gib=4, reps=8):
+    """The device's streaming-read rate (moe_stream_read_probe over `gib` GiB,
+    best of a few grid shapes, median over `reps` reads each): context for the
+    layer's fraction of the 8 TB/s peak."""
+    import numpy as np
+    import torch
+
+    import memory_bound_mxfp4_amd as moe
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = (0.0, 0)
+    for bpc in (2, 4, 8):
+        moe.stream_read_probe(buf, bpc, sink)
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.stream_read_probe(buf, bpc, sink)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        gbps = nbytes / (float(np.median(ts)) * 1e-3) / 1e9
+        if gbps > best[0]:
+            best = (gbps, bpc)
+    del buf
+    return {"gbps": round(best[0], 1), "frac_of_peak": round(best[0] / PEAK_GBPS, 4), "bytes": nbytes,
+            "blocks_per_cu": best[1], "kernel": "k_stream_read (moe_stream_read_probe)"}
+
+
+def dense_gemv_times(batches=(1, 8, 64), mats=8, reps=24):
+    """dense_gemv_bf16 on 7168 x 7168 bf16 matrices (the stack's dense block),
+    rotating over `mats` distinct matrices so none is read from cache; median
+    per-launch event time per batch."""
+    import numpy as np
+    import torch
+
+    import memory_bound_mxfp4_amd as moe
+    import synth
+    from synth import CONFIGS
+    cfg = CONFIGS["k3_stack8"]
+    H = cfg.hidden
+    Ws = []
+    for j in range(mats):
+        t = torch.empty((H, H), dtype=torch.int16, device="cuda")
+        synth.dev_fill_bf16(t, 0, synth.tag(0, synth.KIND_DENSE, 0, j), cfg.weight_sigma)
+        Ws.append(t.view(torch.bfloat16))
+    out = {}
+    for B in batches:
+        x = torch.randn((B, H), device="cuda").to(torch.bfloat16)
+        y = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+        for W in Ws[:2]:
+            moe.dense_gemv_bf16(W, x, y=y)
+        ts = []
+        for i in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.dense_gemv_bf16(Ws[i % mats], x, y=y)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        us = float(np.median(ts))
+        nbytes = H * H * 2 + B * H * 2 * 2
+        out[f"b{B}"] = {"us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    del Ws
+    return out
 
 
 def run_stack(stack, steps, warmup, graph=True, seed=0):
@@ -287,8 +431,9 @@ def main():
     ap.add_argument("--layers", type=int, default=8, help="distinct layer copies rotated across steps")
     ap.add_argument("--variants", type=int, default=32, help="distinct input rows rotated across steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the batch-8 and batch-64 lines")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other batch sizes")
     ap.add_argument("--no-stack", action="store_true", help="skip the 8-layer decode-step stack line")
+    ap.add_argument("--no-probe", action="store_true", help="skip the stream-read ceiling and dense GEMV lines")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the scaled HBM traffic of k_moe_layer from two counter CSVs and exit")
     args = ap.parse_args()
@@ -302,6 +447,7 @@ def main():
         sys.exit(2)
 
     import torch
+    from dataclasses import replace
     from layer_inputs import dense_device, device_weights
     from synth import CONFIGS
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -315,13 +461,16 @@ def main():
     main_r = run_config(cfg, layers[:args.layers], args.steps, args.warmup, args.variants)
     extra = {}
     if not args.no_extra:
-        for name in ("k3_b8", "k3_b64_zipf"):
+        b8 = CONFIGS["k3_b8"]
+        for name, c in (("k3_b4", replace(b8, name="k3_b4", batch=4)), ("k3_b8", b8),
+                        ("k3_b16", replace(b8, name="k3_b16", batch=16)), ("k3_b64_zipf", CONFIGS["k3_b64_zipf"])):
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-            r = run_config(CONFIGS[name], layers[:args.layers], max(10, args.steps // 2), args.warmup, args.variants)
-            extra[name] = {"batch": CONFIGS[name].batch, "us_per_layer": round(r["us_per_layer"], 2),
+            r = run_config(c, layers[:args.layers], max(20, args.steps // 2), args.warmup, args.variants)
+            extra[name] = {"batch": c.batch, "us_per_layer": round(r["us_per_layer"], 2),
                            "gbps": round(r["gbps"], 1), "frac_peak": round(r["gbps"] / PEAK_GBPS, 4),
-                           "distinct_experts": round(r["U_mean"], 1),
-                           "kernel_us": {k: round(v, 2) for k, v in r["kernel_us"].items()}}
+                           "gpu_span_us_per_layer": round(r["gpu_span_us_per_layer"], 2),
+                           "distinct_experts": round(r["U_mean"], 1), "launch_us_events": r["launch_us"],
+                           "validated": r["validated"]}
     if not args.no_stack:
         from memory_bound_mxfp4_amd.stack import DecodeStack
         sc = stack_cfg()
@@ -334,13 +483,20 @@ def main():
                               "frac_peak": round(r["gbps"] / PEAK_GBPS, 4), "bytes_per_step": r["bytes_per_step"],
                               "hip_graph": r["graph"], "kernels_per_step": r["kernels_per_step"]}
         del stack, dense
+    probe = dense = None
+    if not args.no_probe:
+        del layers
+        torch.cuda.empty_cache()
+        print("[bench] stream-read ceiling and dense GEMV", file=sys.stderr, flush=True)
+        probe = stream_ceiling()
+        dense = dense_gemv_times()
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         cpu = cpu_baseline()
-    fc1_bytes = main_r["kernel_bytes"]["k_moe_layer"]
-    fc1_us = main_r["kernel_us"]["k_moe_layer"]
-    achieved = fc1_bytes / (fc1_us * 1e-6) / 1e9
+    kbytes = main_r["kernel_bytes"]["k_moe_layer"]
+    k_us = main_r["gpu_span_us_per_layer"]
+    achieved = kbytes / (k_us * 1e-6) / 1e9
     line = {
         "metric": METRIC,
         "value": round(main_r["gbps"], 1),
@@ -361,13 +517,18 @@ def main():
                                "bf16 router", "batch": 1, "distinct_layers_rotated": args.layers,
                    "input_variants": args.variants, "bytes_per_layer": int(main_r["bytes_per_layer"]),
                    "distinct_experts": round(main_r["U_mean"], 1)},
-        "kernels_per_layer": len(main_r["kernel_us"]),
-        "kernel_us": {k: round(v, 2) for k, v in main_r["kernel_us"].items()},
+        "kernels_per_layer": len(main_r["launch_us"]),
+        "validated": main_r["validated"],
+        "gpu_span_us_per_layer": round(k_us, 2),
+        "launch_us_events": main_r["launch_us"],
         "roofline": {"kernel": "k_moe_layer", "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": recorded_traffic(),
-                     "algorithmic_bytes_per_launch": int(fc1_bytes), "avg_launch_us": round(fc1_us, 2)},
+                     "algorithmic_bytes_per_launch": int(kbytes), "avg_launch_us": round(k_us, 2),
+                     "avg_launch_us_from": "HIP events on the launch stream around the K back-to-back launches, / K",
+                     "stream_read_ceiling": probe},
         "cpu_baseline": cpu,
         "extra_configs": extra,
+        "dense_gemv_7168x7168": dense,
     }
     print(json.dumps(line), flush=True)
 

@@ -200,6 +200,26 @@ moe_status expert_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int n,
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_workspace_status -- enqueue on `stream` a copy of the workspace's
+ * sticky status word (above) into *status, a uint32 in device memory or in
+ * pinned host memory; the value is there once the stream has passed the
+ * call.  0: every synchronisation wait of every call since
+ * moe_workspace_init completed, so their outputs are valid; nonzero: a wait
+ * gave up and the outputs of that call (and of later calls on the
+ * workspace, whose waits then give up at once) are not valid.  A call whose
+ * wait gives up still runs to completion without reading or writing outside
+ * its buffers.  ws 256-byte aligned with ws_bytes covering the control block
+ * (512 bytes); status 4-byte aligned; else MOE_ERR_INVALID_ARGUMENT.
+ */
+moe_status moe_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, void* stream);
+
+/* Batch > 1: the 8 bytes at this workspace offset hold, in their low 32 bits,
+ * the number of distinct experts the last call routed its rows to (counted
+ * on the device from the top-k indices) and, in their high 32 bits, that
+ * call's tag.  Read it after the stream has passed the call. */
+#define MOE_WS_ACTIVE_EXPERTS_OFFSET 384
+
+/*
  * moe_decode_layer -- the whole layer for `batch` rows, as one kernel launch.
  *   x          bf16 [batch][hidden], the layer input (normalised activations)
  *   residual   fp32 [batch][hidden], read and overwritten with
@@ -249,6 +269,19 @@ moe_status dense_gemv_bf16(const uint16_t* w, int n, int k, const uint16_t* x, i
 moe_status residual_add_bf16(float* h, const uint16_t* t, int batch, int hidden, void* stream);
 moe_status residual_add_rmsnorm_bf16(float* h, const uint16_t* t, int batch, int hidden, float eps, uint16_t* out,
                                      void* stream);
+
+/*
+ * moe_stream_read_probe -- measurement aid, not part of a decode step: one
+ * kernel that reads `bytes` of `buf` once with 16-byte non-temporal loads
+ * (blocks_per_cu 256-thread workgroups per compute unit, grid-stride), the
+ * access pattern of a plain streaming read.  Timing it gives the device's
+ * HBM read ceiling that the layer's weight streams are compared with.
+ * `sink` (device, 4 bytes) is written only in the (never expected) case
+ * that the xor of all data equals 0x9E3779B9, so nothing else is stored.
+ * buf 16-byte aligned, bytes a positive multiple of 16, 1 <= blocks_per_cu
+ * <= 32; else MOE_ERR_INVALID_ARGUMENT.
+ */
+moe_status moe_stream_read_probe(const void* buf, size_t bytes, int blocks_per_cu, uint32_t* sink, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);

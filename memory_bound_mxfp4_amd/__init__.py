@@ -26,7 +26,7 @@ EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size"
            "expert_gemv_mxfp4", "moe_decode_layer", "moe_decode_layer_kernel_count",
            "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "moe_pack_experts",
            "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "residual_add_rmsnorm_bf16",
-           "moe_status_string")
+           "moe_workspace_status", "moe_stream_read_probe", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -73,6 +73,8 @@ def load():
         "dense_gemv_bf16": (I, [P, I, I, P, I, P, P]),
         "residual_add_bf16": (I, [P, P, I, I, P]),
         "residual_add_rmsnorm_bf16": (I, [P, P, I, I, F, P, P]),
+        "moe_workspace_status": (I, [P, Z, P, P]),
+        "moe_stream_read_probe": (I, [P, Z, I, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
@@ -190,10 +192,34 @@ def alloc_workspace(w: LayerWeights, batch: int, device=None):
     return workspace_init(ws)
 
 
-def workspace_status(ws) -> int:
-    """The workspace's sticky status word (0 = every wait completed). Synchronises."""
+WS_ACTIVE_EXPERTS_OFFSET = 384
+
+
+def workspace_status(ws, stream=None) -> int:
+    """The workspace's sticky status word (0 = every wait completed), read
+    through moe_workspace_status. Synchronises the stream."""
+    import torch
+    out = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    _check(load().moe_workspace_status(_ptr(ws), ws.numel(), _ptr(out), _stream(stream)), "moe_workspace_status")
+    torch.cuda.synchronize(ws.device)
+    return int(out.item()) & 0xFFFFFFFF
+
+
+def workspace_active_experts(ws) -> int:
+    """Batch > 1: distinct experts the last call on `ws` routed to, as counted
+    on the device (low half of the word at WS_ACTIVE_EXPERTS_OFFSET). Synchronises."""
     import numpy as np
-    return int(ws[WS_STATUS_OFFSET:WS_STATUS_OFFSET + 4].cpu().numpy().view(np.uint32)[0])
+    off = WS_ACTIVE_EXPERTS_OFFSET
+    return int(ws[off:off + 4].cpu().numpy().view(np.uint32)[0])
+
+
+def stream_read_probe(buf, blocks_per_cu: int = 4, sink=None, stream=None):
+    """Enqueue one streaming read of all of `buf` (moe_stream_read_probe)."""
+    import torch
+    sink = torch.zeros(1, dtype=torch.int32, device=buf.device) if sink is None else sink
+    _check(load().moe_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), blocks_per_cu, _ptr(sink),
+                                        _stream(stream)), "moe_stream_read_probe")
+    return sink
 
 
 def router_topk(x, router_w, top_k: int, bias=None, idx=None, gate=None, logits=None, ws=None, stream=None):

@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SO = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["api.hip", "router.hip", "experts.hip", "dense.hip", "pack.hip", "layer.hip"]
+SOURCES = ["api.hip", "router.hip", "experts.hip", "dense.hip", "pack.hip", "layer.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU ops are disabled for all device code.  The atomic
 # optimizer is off: it rewrites a one-lane atomic into a wave-wide pattern

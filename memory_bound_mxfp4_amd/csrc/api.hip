@@ -242,6 +242,23 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return MOE_OK;
 }
 
+moe_status moe_workspace_status(const void* ws, size_t ws_bytes, uint32_t* status, void* stream) {
+  if (!ws || !status || !aligned(ws, 256) || !aligned(status, 4) || ws_bytes < sizeof(unsigned) * CTRL_WORDS)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const char* word = static_cast<const char*>(ws) + MOE_WS_STATUS_OFFSET;
+  if (hipMemcpyAsync(status, word, sizeof(uint32_t), hipMemcpyDefault, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_stream_read_probe(const void* buf, size_t bytes, int blocks_per_cu, uint32_t* sink, void* stream) {
+  if (!buf || !sink || !aligned(buf, 16) || bytes < 16 || bytes % 16 || blocks_per_cu < 1 || blocks_per_cu > 32)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (launch_stream_read(buf, bytes, blocks_per_cu, sink, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 moe_status rmsnorm_bf16(const float* in, int batch, int hidden, float eps, uint16_t* out, void* stream) {
   if (!in || !out || batch < 1 || batch > MOE_MAX_BATCH || hidden < 1 || !(eps >= 0.0f))
     return MOE_ERR_INVALID_ARGUMENT;

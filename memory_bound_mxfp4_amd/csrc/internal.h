@@ -97,6 +97,8 @@ hipError_t launch_residual_add(float* h, const uint16_t* t, int B, int H, hipStr
 hipError_t launch_residual_add_rmsnorm(float* h, const uint16_t* t, int B, int H, float eps, uint16_t* out,
                                        hipStream_t s);
 
+hipError_t launch_stream_read(const void* buf, size_t bytes, int blocks_per_cu, uint32_t* sink, hipStream_t s);
+
 int num_cus();
 
 }  // namespace moe

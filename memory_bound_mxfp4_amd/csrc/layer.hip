@@ -132,6 +132,7 @@ struct Lds {  // static LDS of the kernel
   int next;        // next unit index (first claim)
   int nxt[2];      // next unit index, alternating between iterations of the unit loop
   int U;           // distinct experts (once known)
+  int sched_ok;    // batch > 1: the schedule's ready word arrived
   int wtot[12];    // scan scratch
   int nrows;       // rows of the current unit
   float gates[MOE_MAX_TOPK];  // combine: gates of the current row
@@ -151,20 +152,19 @@ struct WgState {
 };
 
 // Bounded poll of one control word until it has `tag` in its high half
-// (thread 0 only); returns the low half.
-__device__ __forceinline__ uint32_t poll_ready(const LayerParams& p, uint32_t tag) {
+// (thread 0 only).  Returns the low half, or -1 if the wait gave up (the
+// sticky error word is then set).
+__device__ __forceinline__ int poll_ready(const LayerParams& p, uint32_t tag) {
   const uint64_t* a = reinterpret_cast<const uint64_t*>(p.ctrl + CTRL_READY);
-  uint64_t v;
   for (unsigned it = 0;; ++it) {
-    v = ld_pair(a);
-    if (pair_has(v, tag)) break;
+    const uint64_t v = ld_pair(a);
+    if (pair_has(v, tag)) return (int)min((uint32_t)v, 0x7FFFFFFFu);
     if (it >= SPIN_LIMIT || ((it & 255) == 255 && ld_coh(p.ctrl + CTRL_ERR) != 0u)) {
       set_error(p);
-      break;
+      return -1;
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  return (uint32_t)v;
 }
 
 // The schedule into this workgroup's LDS.  Batch 1: one row, so slot j is
@@ -192,28 +192,44 @@ __device__ __forceinline__ void cache_schedule(const LayerParams& p, WgState& st
       L.U = p.k;
     }
   } else {
-    if (TID_ == 0) L.U = (int)min(poll_ready(p, st.tag), (uint32_t)p.umax);
+    if (TID_ == 0) {
+      const int u = poll_ready(p, st.tag);
+      L.sched_ok = u >= 0;
+      L.U = u < 0 ? 0 : min(u, p.umax);
+    }
     __syncthreads();
     const int U = L.U, nslots = p.B * p.k;
-    const int total = U + (U + 1) + nslots + (U + 1);
-    for (int base = TID_; base < total; base += 256 * 8) {
-      int v[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int i = min(base + 256 * t, total - 1);
-        v[t] = i < U ? ld_coh(p.active + i)
-                     : (i < 2 * U + 1 ? ld_coh(p.row_off + (i - U))
-                                      : (i < 2 * U + 1 + nslots ? ld_coh(p.rows + (i - 2 * U - 1))
-                                                                : ld_coh(p.cg_off + (i - 2 * U - 1 - nslots))));
+    if (!L.sched_ok) {
+      // The schedule never arrived (the call's outputs are invalid and the
+      // status word says so): no active experts, so no routed unit reads an
+      // expert, a row list or a flag that this call did not write.
+      if (TID_ == 0) {
+        ro[0] = 0;
+        cgo[0] = 0;
       }
+    } else {
+      // Published before the ready word, so consistent; the clamps only keep
+      // every later index inside its buffer whatever the memory holds.
+      const int total = U + (U + 1) + nslots + (U + 1);
+      for (int base = TID_; base < total; base += 256 * 8) {
+        int v[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int i = base + 256 * t;
-        if (i < total) {
-          if (i < U) a[i] = v[t];
-          else if (i < 2 * U + 1) ro[i - U] = v[t];
-          else if (i < 2 * U + 1 + nslots) rw[i - 2 * U - 1] = v[t];
-          else cgo[i - 2 * U - 1 - nslots] = v[t];
+        for (int t = 0; t < 8; ++t) {
+          const int i = min(base + 256 * t, total - 1);
+          v[t] = i < U ? ld_coh(p.active + i)
+                       : (i < 2 * U + 1 ? ld_coh(p.row_off + (i - U))
+                                        : (i < 2 * U + 1 + nslots ? ld_coh(p.rows + (i - 2 * U - 1))
+                                                                  : ld_coh(p.cg_off + (i - 2 * U - 1 - nslots))));
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int i = base + 256 * t;
+          if (i < total) {
+            if (i < U) a[i] = min(max(v[t], 0), p.E - 1);
+            else if (i < 2 * U + 1) ro[i - U] = min(max(v[t], 0), nslots);
+            else if (i < 2 * U + 1 + nslots) rw[i - 2 * U - 1] = min(max(v[t], 0), nslots - 1);
+            else cgo[i - 2 * U - 1 - nslots] = min(max(v[t], 0), 4 * U);
+          }
         }
       }
     }
@@ -1852,12 +1868,12 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
         const int NCG = st.s_cg_off[U];  // column groups of all active experts
         if (rel < NCG * p.mf_t1) {
           const int gc = rel / p.mf_t1, ae = find_expert(st, gc);
-          mf_fc1_unit<true, FULL>(p, st, L, mfb, ae, gc - st.s_cg_off[ae], rel % p.mf_t1);
+          mf_fc1_unit<true, FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t1);
         } else if ((rel -= NCG * p.mf_t1) < p.n_s2) {
           mf_fc2_unit<false, FULL>(p, st, L, mfb, -1, rel / p.mf_t2s, rel % p.mf_t2s);
         } else if ((rel -= p.n_s2) < NCG * p.mf_t2) {
           const int gc = rel / p.mf_t2, ae = find_expert(st, gc);
-          mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, gc - st.s_cg_off[ae], rel % p.mf_t2);
+          mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t2);
         } else if ((rel -= NCG * p.mf_t2) < p.B * p.n_tile) {
           combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile);
         } else {

@@ -23,11 +23,12 @@ _lib = None
 
 
 def build() -> str:
-    """Compile oracle.cpp into liboracle.so (plain g++, single thread)."""
+    """Compile oracle.cpp into liboracle.so (plain g++; OpenMP spreads a layer's
+    independent expert evaluations over host threads)."""
     src = os.path.join(_DIR, "oracle.cpp")
     tmp = _SO + ".tmp"
     subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
-                           "-fno-fast-math", src, "-o", tmp])
+                           "-fno-fast-math", "-fopenmp", src, "-o", tmp])
     os.replace(tmp, _SO)
     return _SO
 
@@ -54,6 +55,7 @@ def _load():
         "oracle_to_bf16": (None, [P, U64, P]),
         "oracle_rmsnorm_bf16": (None, [P, I, I, D, P]),
         "oracle_dense_gemv_bf16": (None, [P, I, I, P, I, P]),
+        "oracle_set_threads": (I, [I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -167,6 +169,12 @@ def moe_layer(H, I, E, k, Is, router_w, router_bias, shared_gate, shared_up, sha
     if want_stages:
         res.update(logits=logits, shared=shared, slots=slots)
     return res
+
+
+def set_threads(n: int = 0) -> int:
+    """Host threads for the layer's expert evaluations (0: leave as is);
+    returns the number in effect.  Results do not depend on it."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 def to_bf16(a):

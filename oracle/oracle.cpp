@@ -31,6 +31,9 @@
 #include <cstdint>
 #include <cstring>
 #include <vector>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 namespace {
 
@@ -251,24 +254,46 @@ int oracle_moe_layer(int H, int I, int E, int k, int Is, const uint16_t* router_
   int od = oracle_router_logits(x, router_w, router_bias, B, H, E, logits.data());
   oracle_topk(logits.data(), B, E, k, idx, gate);
   if (logits_out) std::memcpy(logits_out, logits.data(), sizeof(float) * logits.size());
-  std::vector<float> os((size_t)H, 0.0f), oj((size_t)k * H);
-  for (int b = 0; b < B; ++b) {
+  for (int s = 0; s < B * k; ++s)
+    if (!experts[idx[s]]) return -1;
+  // The expert evaluations of the B rows (k routed + 1 shared each) are
+  // independent of each other; they may run on several host threads
+  // (oracle_set_threads), each evaluation exactly as on one thread.
+  std::vector<float> os((size_t)B * H, 0.0f), oj((size_t)B * k * H);
+  const int per_row = k + 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < B * per_row; ++t) {
+    const int b = t / per_row, j = t % per_row;
     const uint16_t* xb = x + (size_t)b * H;
-    if (Is > 0) oracle_shared_expert(shared_gate, shared_up, shared_down, H, Is, xb, 1, os.data());
-    for (int j = 0; j < k; ++j) {
-      const uint8_t* blob = experts[idx[(size_t)b * k + j]];
-      if (!blob) return -1;
-      oracle_routed_expert(blob, H, I, xb, 1, oj.data() + (size_t)j * H);
+    if (j == k) {
+      if (Is > 0) oracle_shared_expert(shared_gate, shared_up, shared_down, H, Is, xb, 1, os.data() + (size_t)b * H);
+    } else {
+      oracle_routed_expert(experts[idx[(size_t)b * k + j]], H, I, xb, 1, oj.data() + ((size_t)b * k + j) * H);
     }
+  }
+  for (int b = 0; b < B; ++b) {
+    const float* ob = oj.data() + (size_t)b * k * H;
     for (int m = 0; m < H; ++m) {
-      double acc = (double)residual[(size_t)b * H + m] + (double)os[m];
-      for (int j = 0; j < k; ++j) acc += (double)gate[(size_t)b * k + j] * (double)oj[(size_t)j * H + m];
+      double acc = (double)residual[(size_t)b * H + m] + (double)os[(size_t)b * H + m];
+      for (int j = 0; j < k; ++j) acc += (double)gate[(size_t)b * k + j] * (double)ob[(size_t)j * H + m];
       out[(size_t)b * H + m] = (float)acc;
     }
-    if (shared_out) std::memcpy(shared_out + (size_t)b * H, os.data(), sizeof(float) * H);
-    if (slot_out) std::memcpy(slot_out + (size_t)b * k * H, oj.data(), sizeof(float) * (size_t)k * H);
+    if (shared_out) std::memcpy(shared_out + (size_t)b * H, os.data() + (size_t)b * H, sizeof(float) * H);
+    if (slot_out) std::memcpy(slot_out + (size_t)b * k * H, ob, sizeof(float) * (size_t)k * H);
   }
   return od;
+}
+
+// Host threads the layer's expert evaluations may use (OpenMP); the results
+// do not depend on it.  Returns the number now in effect.
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
 }
 
 // ---- dense block pieces of the layer stack ----------------------------------

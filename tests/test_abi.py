@@ -128,3 +128,15 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.dense_gemv_bf16(P(0x1000), 16, 12, x, 1, P(0x3000), None) == -1
     assert lib.rmsnorm_bf16(None, 1, 16, ctypes.c_float(1e-6), P(0x3000), None) == -1
     assert lib.residual_add_bf16(P(0x1000), None, 1, 16, None) == -1
+    # workspace status: NULL, misaligned, a buffer smaller than the control block
+    assert lib.moe_workspace_status(None, 4096, P(0x3000), None) == -1
+    assert lib.moe_workspace_status(ws, 4096, None, None) == -1
+    assert lib.moe_workspace_status(P(0x100010), 4096, P(0x3000), None) == -1
+    assert lib.moe_workspace_status(ws, 256, P(0x3000), None) == -1
+    assert lib.moe_workspace_status(ws, 4096, P(0x3002), None) == -1
+    # stream-read probe: NULL, size not a multiple of 16, grid shape outside 1..32 blocks per CU
+    assert lib.moe_stream_read_probe(None, 1 << 20, 4, P(0x3000), None) == -1
+    assert lib.moe_stream_read_probe(P(0x1000), 1000, 4, P(0x3000), None) == -1
+    assert lib.moe_stream_read_probe(P(0x1000), 1 << 20, 0, P(0x3000), None) == -1
+    assert lib.moe_stream_read_probe(P(0x1000), 1 << 20, 33, P(0x3000), None) == -1
+    assert lib.moe_stream_read_probe(P(0x1000), 1 << 20, 4, None, None) == -1

@@ -127,9 +127,11 @@ def test_k3_batch8(k3_layer):
     _check(cfg, 0, x, res, out, idx, gate)
 
 
+@pytest.mark.timeout(900)
 def test_k3_batch64_zipf(k3_layer):
-    """Full-size batch 64 with the Zipf-like bias: every row's indices are
-    compared; outputs are compared on sampled rows."""
+    """Full-size batch 64 with the Zipf-like bias: every row's indices, gates
+    and outputs against the oracle (the oracle's expert evaluations spread
+    over the host's cores)."""
     import torch
     cfg = CONFIGS["k3_b64_zipf"]
     print("[case] layer K3 B64 zipf seed 0", flush=True)
@@ -148,14 +150,15 @@ def test_k3_batch64_zipf(k3_layer):
     assert np.abs(gate - gate_ref).max() <= 1e-6
     counts = np.bincount(idx.ravel(), minlength=cfg.num_experts)
     print(f"    distinct experts {int((counts > 0).sum())}, hottest {int(counts.max())} rows", flush=True)
-    _check(cfg, 0, x, res, out, idx, gate, rows=[0, 31, 63])
+    _check(cfg, 0, x, res, out, idx, gate)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("B", [4, 16, 33])
 def test_k3_verify_and_ragged_batches(k3_layer, B):
     """Verify-step batch shapes (4 and 16 rows) and a ragged one (33 rows: a
     partial router row block and a one-row column group): every row's
-    indices and gates against the oracle, outputs on the first and last row."""
+    indices, gates and outputs against the oracle."""
     cfg = CONFIGS["k3_b8"]
     print(f"[case] layer K3 B{B} seed 0", flush=True)
     x = x_host(cfg, 0, variant=5, batch=B)
@@ -166,7 +169,7 @@ def test_k3_verify_and_ragged_batches(k3_layer, B):
     idx_ref, gate_ref = oracle.topk(lg, cfg.top_k)
     assert np.array_equal(idx, idx_ref)
     assert np.abs(gate - gate_ref).max() <= 1e-6
-    _check(cfg, 0, x, res, out, idx, gate, rows=[0, B - 1])
+    _check(cfg, 0, x, res, out, idx, gate)
 
 
 def test_k3_deterministic(k3_layer):
@@ -184,6 +187,32 @@ def test_k3_deterministic(k3_layer):
         if first is None:
             first = out
         assert np.array_equal(out.view(np.uint32), first.view(np.uint32))
+
+
+def test_k3_deterministic_batch64_zipf(k3_layer):
+    """50 calls of the batch-64 Zipf layer on one workspace (the hottest
+    expert's rows spread over four column groups, ~240 active experts): every
+    call bit-identical to the first, and no wait gave up."""
+    import torch
+    cfg = CONFIGS["k3_b64_zipf"]
+    print("[case] layer K3 B64 zipf determinism x50", flush=True)
+    k3_layer.router_bias = _dev(synth.zipf_bias(0, 0, cfg.num_experts, cfg.zipf_s))
+    try:
+        x = _dev(x_host(cfg, 0, variant=4))
+        res0 = _dev(residual_from_x(x_host(cfg, 0, variant=4)))
+        ws = moe.alloc_workspace(k3_layer, 64)
+        first = None
+        for it in range(50):
+            r = res0.clone()
+            idx, _ = moe.moe_decode_layer(k3_layer, x, r, ws=ws)
+            torch.cuda.synchronize()
+            if first is None:
+                first = (r.view(torch.int32).clone(), idx.clone())
+            else:
+                assert torch.equal(r.view(torch.int32), first[0]) and torch.equal(idx, first[1]), it
+        assert moe.workspace_status(ws) == 0
+    finally:
+        k3_layer.router_bias = None
 
 
 def test_workspace_reuse_and_status(k3_layer):
@@ -250,3 +279,30 @@ def test_timed_entry_point_matches_untimed():
     torch.cuda.synchronize()
     assert np.array_equal(r.cpu().numpy(), out) and np.array_equal(idx2.cpu().numpy(), idx)
     assert all(events[i].elapsed_time(events[i + 1]) >= 0 for i in range(len(names)))
+
+
+def test_k3_batch8_device_union_count(k3_layer):
+    """Distinct experts per verify step, as counted on the device by the
+    schedule, equal the count from the returned indices on every call, and
+    their mean over 24 independent 8-row batches lies within 5% of the union
+    model 896 (1 - (880/896)^8) ~ 120.3 ("Kimi K3 on GB300", section "What
+    DSpark adds": rows of a verify step route independently)."""
+    import torch
+    cfg = CONFIGS["k3_b8"]
+    print("[case] layer K3 B8 device-counted distinct experts x24", flush=True)
+    ws = moe.alloc_workspace(k3_layer, 8)
+    counts = []
+    for v in range(24):
+        x = x_host(cfg, 0, variant=100 + v)
+        r = _dev(residual_from_x(x))
+        idx, _ = moe.moe_decode_layer(k3_layer, _dev(x), r, ws=ws)
+        torch.cuda.synchronize()
+        u_dev = moe.workspace_active_experts(ws)
+        u_idx = int(np.unique(idx.cpu().numpy()).size)
+        assert u_dev == u_idx, (v, u_dev, u_idx)
+        counts.append(u_dev)
+    assert moe.workspace_status(ws) == 0
+    model = 896 * (1 - (880 / 896) ** 8)
+    mean = float(np.mean(counts))
+    print(f"    mean distinct experts {mean:.2f} (model {model:.2f})", flush=True)
+    assert abs(mean - model) <= 0.05 * model

@@ -197,6 +197,22 @@ def test_layer_stages_and_residual_and_no_shared():
     assert np.allclose(r3["out"], ref, rtol=1e-6, atol=1e-7)
 
 
+def test_layer_same_result_on_one_or_many_threads():
+    """The layer's expert evaluations may run on several host threads: the
+    result is bit-identical to one thread's."""
+    L = _tiny_layer(5)
+    n0 = oracle.set_threads(0)
+    try:
+        oracle.set_threads(1)
+        r1 = _run(L)
+        oracle.set_threads(max(2, n0))
+        rn = _run(L)
+    finally:
+        oracle.set_threads(n0)
+    for key in ("out", "idx", "gate", "shared", "slots"):
+        assert np.array_equal(r1[key].view(np.uint8), rn[key].view(np.uint8)), key
+
+
 def test_layer_missing_expert_blob_is_an_error():
     L = _tiny_layer(4)
     with pytest.raises(ValueError):
