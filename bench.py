@@ -432,6 +432,8 @@ def main():
     ap.add_argument("--variants", type=int, default=32, help="distinct input rows rotated across steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other batch sizes")
+    ap.add_argument("--extra", default="k3_b4,k3_b8,k3_b16,k3_b64_zipf",
+                    help="comma-separated other batch configurations to time")
     ap.add_argument("--no-stack", action="store_true", help="skip the 8-layer decode-step stack line")
     ap.add_argument("--no-probe", action="store_true", help="skip the stream-read ceiling and dense GEMV lines")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -462,8 +464,11 @@ def main():
     extra = {}
     if not args.no_extra:
         b8 = CONFIGS["k3_b8"]
+        wanted = set(args.extra.split(","))
         for name, c in (("k3_b4", replace(b8, name="k3_b4", batch=4)), ("k3_b8", b8),
                         ("k3_b16", replace(b8, name="k3_b16", batch=16)), ("k3_b64_zipf", CONFIGS["k3_b64_zipf"])):
+            if name not in wanted:
+                continue
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
             r = run_config(c, layers[:args.layers], max(20, args.steps // 2), args.warmup, args.variants)
             extra[name] = {"batch": c.batch, "us_per_layer": round(r["us_per_layer"], 2),
