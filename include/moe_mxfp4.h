@@ -237,6 +237,34 @@ moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float
                             int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_decode_layer_noalloc -- moe_decode_layer for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It takes no workspace: the library's
+ * own static device array of MOE_NOALLOC_SCRATCH_BYTES serves instead, one
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * call itself allocates nothing.  x, residual, topk_idx, topk_gate and w are
+ * as for moe_decode_layer.
+ *   status   device pointer to a uint32 (or NULL): after the layer, the
+ *            array's sticky status word is copied there on `stream` (0: every
+ *            wait of every no-allocation call on this GPU completed, see
+ *            moe_workspace_status)
+ * Errors: MOE_ERR_WORKSPACE_TOO_SMALL, before anything is enqueued, when
+ * moe_workspace_size(w, batch) exceeds MOE_NOALLOC_SCRATCH_BYTES (24 MiB:
+ * the K3 shape fits up to batch 20); MOE_ERR_UNSUPPORTED when the first call
+ * on a GPU is made while `stream` is being captured (that call clears the
+ * array once with a fill kernel, which must not be recorded into a graph);
+ * otherwise as moe_decode_layer.
+ * Every call on one GPU shares that GPU's array and leaves its contents for
+ * the next (each call's data carries that call's tag, so nothing stale is
+ * ever taken as current): calls on one GPU must be ordered -- two that
+ * overlap, on different streams or threads, race on the array and their
+ * results are undefined.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (24u << 20)
+moe_status moe_decode_layer_noalloc(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                                    int32_t* topk_idx, float* topk_gate, uint32_t* status, void* stream);
+
+/*
  * Per-kernel timing of moe_decode_layer (for profiling and benchmarks).
  * moe_decode_layer_kernel_count() is the number K of kernels one call
  * launches; moe_decode_layer_kernel_name(i) the name of the i-th (NULL out

@@ -26,7 +26,7 @@ EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size"
            "expert_gemv_mxfp4", "moe_decode_layer", "moe_decode_layer_kernel_count",
            "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "moe_pack_experts",
            "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "residual_add_rmsnorm_bf16",
-           "moe_workspace_status", "moe_stream_read_probe", "moe_status_string")
+           "moe_workspace_status", "moe_stream_read_probe", "moe_decode_layer_noalloc", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +74,7 @@ def load():
         "residual_add_bf16": (I, [P, P, I, I, P]),
         "residual_add_rmsnorm_bf16": (I, [P, P, I, I, F, P, P]),
         "moe_workspace_status": (I, [P, Z, P, P]),
+        "moe_decode_layer_noalloc": (I, [P, P, P, I, P, P, P, P]),
         "moe_stream_read_probe": (I, [P, Z, I, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
     }
@@ -260,6 +261,20 @@ def moe_decode_layer(w: LayerWeights, x, residual, idx=None, gate=None, ws=None,
     cs = w.c_struct()
     _check(load().moe_decode_layer(ctypes.byref(cs), _ptr(x), _ptr(residual), B, _ptr(idx), _ptr(gate), _ptr(ws),
                                    ws.numel(), _stream(stream)), "moe_decode_layer")
+    return idx, gate
+
+
+NOALLOC_SCRATCH_BYTES = 24 << 20
+
+
+def moe_decode_layer_noalloc(w: LayerWeights, x, residual, idx, gate, status=None, stream=None):
+    """moe_decode_layer on the library's own static device workspace
+    (moe_decode_layer_noalloc): nothing is allocated by the call.  idx, gate
+    and the optional status word (int32 [1]) are caller-provided device tensors."""
+    B = x.shape[0]
+    cs = w.c_struct()
+    _check(load().moe_decode_layer_noalloc(ctypes.byref(cs), _ptr(x), _ptr(residual), B, _ptr(idx), _ptr(gate),
+                                           _ptr(status), _stream(stream)), "moe_decode_layer_noalloc")
     return idx, gate
 
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "internal.h"
 #include "moe_mxfp4.h"
@@ -194,6 +195,66 @@ moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float
                             int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
   return run_layer(w, x, residual, batch, topk_idx, topk_gate, ws, ws_bytes, static_cast<hipStream_t>(stream),
                    nullptr);
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing ---------------------------------
+//
+// Its workspace is this file-scope device array: every GPU the library runs
+// on holds its own copy from the first call until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the device
+// address of each GPU's copy is looked up once, with that GPU current, and
+// only that address is ever handed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];  // per device: device address of `scratch`, once set up
+
+// The current device's copy of `scratch`, set up on its first use: address
+// looked up, then the whole array cleared by a fill kernel on `s` (the
+// control block at its start must begin at zero, and no stale pair may
+// carry a tag a later call could take for its own).  That first use must not
+// be under stream capture, where the fill would be recorded into the graph.
+static moe_status noalloc_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  if (dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return MOE_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return MOE_ERR_UNSUPPORTED;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    if (launch_zero(ptr, MOE_NOALLOC_SCRATCH_BYTES, s) != hipSuccess) return MOE_ERR_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_decode_layer_noalloc(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                                    int32_t* topk_idx, float* topk_gate, uint32_t* status, void* stream) {
+  moe_status st = check_layer(w, batch);
+  if (st != MOE_OK) return st;
+  if (status && !aligned(status, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = ws_layout(nullptr, w->hidden, w->inter, w->num_experts, w->top_k, w->shared_inter, batch).bytes;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!x || !residual || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = noalloc_scratch(s, &ws);
+  if (st != MOE_OK) return st;
+  st = run_layer(w, x, residual, batch, topk_idx, topk_gate, ws, MOE_NOALLOC_SCRATCH_BYTES, s, nullptr);
+  if (st != MOE_OK || !status) return st;
+  if (hipMemcpyAsync(status, static_cast<const char*>(ws) + MOE_WS_STATUS_OFFSET, sizeof(uint32_t),
+                     hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 int moe_decode_layer_kernel_count(void) { return kNumLayerKernels; }
