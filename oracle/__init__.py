@@ -56,6 +56,11 @@ def _load():
         "oracle_rmsnorm_bf16": (None, [P, I, I, D, P]),
         "oracle_dense_gemv_bf16": (None, [P, I, I, P, I, P]),
         "oracle_set_threads": (I, [I]),
+        "oracle_e4m3": (D, [I]),
+        "oracle_quantize_mxfp8": (None, [P, I, P, P]),
+        "oracle_dequantize_mxfp8": (None, [P, P, I, P]),
+        "oracle_routed_expert_ex": (None, [P, I, I, P, I, P, I]),
+        "oracle_moe_layer_ex": (I, [I, I, I, I, I, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -129,16 +134,38 @@ def shared_expert(wg, wu, wd, H, Is, x):
     return out
 
 
-def routed_expert(blob, H, I, x):
+def routed_expert(blob, H, I, x, mx8=False):
+    """One routed MXFP4 expert on rows x (bf16 bits); mx8: the FP4 x MXFP8 variant."""
     x = _c(x, np.uint16).reshape(-1, H)
     out = np.empty((x.shape[0], H), np.float32)
-    _load().oracle_routed_expert(_p(_c(blob, np.uint8)), H, I, _p(x), x.shape[0], _p(out))
+    _load().oracle_routed_expert_ex(_p(_c(blob, np.uint8)), H, I, _p(x), x.shape[0], _p(out), int(bool(mx8)))
     return out
 
 
+def e4m3(code: int) -> float:
+    return _load().oracle_e4m3(int(code))
+
+
+def quantize_mxfp8(v):
+    """MXFP8 quantisation of float32 values (length a multiple of 32): (codes uint8, scales uint8)."""
+    v = _c(v, np.float32).ravel()
+    codes = np.empty(v.size, np.uint8)
+    scales = np.empty(v.size // 32, np.uint8)
+    _load().oracle_quantize_mxfp8(_p(v), v.size, _p(codes), _p(scales))
+    return codes, scales
+
+
+def dequantize_mxfp8(codes, scales):
+    codes, scales = _c(codes, np.uint8).ravel(), _c(scales, np.uint8).ravel()
+    v = np.empty(codes.size, np.float32)
+    _load().oracle_dequantize_mxfp8(_p(codes), _p(scales), codes.size, _p(v))
+    return v
+
+
 def moe_layer(H, I, E, k, Is, router_w, router_bias, shared_gate, shared_up, shared_down, experts, x, residual,
-              want_stages=False):
+              want_stages=False, mx8=False):
     """experts: mapping expert id -> uint8 blob (only selected experts are needed).
+    mx8: the routed experts run the FP4 x MXFP8 variant.
 
     Returns dict(out, idx, gate, order_dependent[, logits, shared, slots]).
     """
@@ -160,9 +187,9 @@ def moe_layer(H, I, E, k, Is, router_w, router_bias, shared_gate, shared_up, sha
     sg = None if shared_gate is None else _c(shared_gate, np.uint16)
     su = None if shared_up is None else _c(shared_up, np.uint16)
     sd = None if shared_down is None else _c(shared_down, np.uint16)
-    rc = _load().oracle_moe_layer(H, I, E, k, Is, _p(rw), _p(rb), _p(sg), _p(su), _p(sd),
-                                  ctypes.cast(table, ctypes.c_void_p), _p(x), _p(residual), B, _p(out), _p(idx),
-                                  _p(gate), _p(logits), _p(shared), _p(slots))
+    rc = _load().oracle_moe_layer_ex(H, I, E, k, Is, _p(rw), _p(rb), _p(sg), _p(su), _p(sd),
+                                     ctypes.cast(table, ctypes.c_void_p), _p(x), _p(residual), B, _p(out), _p(idx),
+                                     _p(gate), _p(logits), _p(shared), _p(slots), int(bool(mx8)))
     if rc < 0:
         raise ValueError("oracle_moe_layer: a selected expert has no blob")
     res = dict(out=out, idx=idx, gate=gate, order_dependent=rc)

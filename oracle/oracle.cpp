@@ -94,6 +94,65 @@ double oracle_e8m0(int byte) {
   return std::ldexp(1.0, byte - 127);
 }
 
+// ---- MXFP8 activations (OCP MX v1.0, E4M3 elements) ----------------------
+//
+// The opt-in variant of the layer quantises the routed experts' activations
+// to MXFP8, the precision "Kimi K3 on GB300: 13 kernels a layer, and what 842
+// and 423 tokens a second measure" (section "Why batch 1 on a rack is not
+// only a bandwidth problem") gives for its expert kernel: FP4 weights times
+// MXFP8 activations.  E4M3 (OCP 8-bit floating point, the "FN" variant the
+// MX formats use): sign, 4-bit exponent with bias 7, 3-bit mantissa; exponent
+// field 0 holds the subnormals m/8 * 2^-6; S.1111.111 is NaN; there is no
+// infinity; the largest finite magnitude is 1.75 * 2^8 = 448.
+double oracle_e4m3(int code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return std::nan("");
+  double mag = (e == 0) ? std::ldexp((double)m / 8.0, -6) : std::ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+// Nearest E4M3 code to v (ties to the even code), magnitudes past the
+// largest finite one clamped to it (saturation).  v finite.
+static int e4m3_encode(double v) {
+  int s = std::signbit(v) ? 1 : 0;
+  double a = std::fabs(v);
+  int best = 0;
+  double best_d = a;  // code 0 (+0)
+  for (int c = 1; c < 0x7F; ++c) {  // the finite non-negative codes, ascending
+    double d = std::fabs(oracle_e4m3(c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (s << 7) | best;
+}
+
+// MXFP8 quantisation of n values (n a multiple of 32), block by block of 32
+// consecutive values: the shared scale is X = 2^(floor(log2(amax)) - 8), 8
+// being the exponent of E4M3's largest power of two, clamped to the E8M0
+// range [2^-127, 2^127] (amax = 0 gives 2^-127); each element is the E4M3
+// code nearest v / X.  scales[i] is the E8M0 byte of block i.
+void oracle_quantize_mxfp8(const float* v, int n, uint8_t* codes, uint8_t* scales) {
+  for (int b = 0; b < n / 32; ++b) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs((double)v[32 * b + i]));
+    int e = -127;
+    if (amax > 0.0) {
+      int ex;
+      std::frexp(amax, &ex);  // amax = f * 2^ex, 0.5 <= f < 1: floor(log2 amax) = ex - 1
+      e = std::min(127, std::max(-127, ex - 1 - 8));
+    }
+    scales[b] = (uint8_t)(e + 127);
+    for (int i = 0; i < 32; ++i) codes[32 * b + i] = (uint8_t)e4m3_encode(std::ldexp((double)v[32 * b + i], -e));
+  }
+}
+
+// The values an MXFP8 block encodes: e4m3(code) * 2^(scale - 127).
+void oracle_dequantize_mxfp8(const uint8_t* codes, const uint8_t* scales, int n, float* v) {
+  for (int i = 0; i < n; ++i) v[i] = (float)(oracle_e4m3(codes[i]) * oracle_e8m0(scales[i / 32]));
+}
+
 // Byte size of one expert blob: gate codes [I][H/2], up codes [I][H/2],
 // down codes [H][I/2], gate scales [I][H/32], up scales [I][H/32],
 // down scales [H][I/32], each sub-array starting on a 256-byte boundary.
@@ -182,18 +241,32 @@ void oracle_topk(const float* logits, int B, int E, int k, int32_t* idx, float* 
 }  // extern "C"
 
 // One SwiGLU expert on one activation row, weights given as callables.
+// With mx8, the routed experts' FP4 x MXFP8 variant: the row entering FC1
+// and the SwiGLU output entering FC2 are each replaced by their MXFP8
+// quantisation (oracle_quantize_mxfp8) before the dot products.
 template <class WG, class WU, class WD>
-static void swiglu_expert(int H, int I, const uint16_t* xrow, WG wg, WU wu, WD wd, float* o) {
-  std::vector<float> h(I);
+static void swiglu_expert(int H, int I, const uint16_t* xrow, WG wg, WU wu, WD wd, float* o, bool mx8 = false) {
+  std::vector<float> xin(H), h(I);
+  for (int k = 0; k < H; ++k) xin[k] = (float)bf16_to_double(xrow[k]);
+  if (mx8) {
+    std::vector<uint8_t> c(H), sc(H / 32);
+    oracle_quantize_mxfp8(xin.data(), H, c.data(), sc.data());
+    oracle_dequantize_mxfp8(c.data(), sc.data(), H, xin.data());
+  }
   for (int n = 0; n < I; ++n) {
     double g = 0.0, u = 0.0;
     for (int k = 0; k < H; ++k) {
-      double xv = bf16_to_double(xrow[k]);
+      double xv = (double)xin[k];
       g += wg(n, k) * xv;
       u += wu(n, k) * xv;
     }
     float gf = (float)g, uf = (float)u;
     h[n] = (float)(silu((double)gf) * (double)uf);
+  }
+  if (mx8) {
+    std::vector<uint8_t> c(I), sc(I / 32);
+    oracle_quantize_mxfp8(h.data(), I, c.data(), sc.data());
+    oracle_dequantize_mxfp8(c.data(), sc.data(), I, h.data());
   }
   for (int m = 0; m < H; ++m) {
     double acc = 0.0;
@@ -228,14 +301,20 @@ static Blob blob_view(const uint8_t* base, int H, int I) {
   return bl;
 }
 
-// One routed MXFP4 expert (blob layout of oracle_expert_bytes) on x[b].
-void oracle_routed_expert(const uint8_t* blob, int H, int I, const uint16_t* x, int B, float* out) {
+// One routed MXFP4 expert (blob layout of oracle_expert_bytes) on x[b];
+// mx8 != 0: its activations quantised to MXFP8 (see swiglu_expert).
+void oracle_routed_expert_ex(const uint8_t* blob, int H, int I, const uint16_t* x, int B, float* out, int mx8) {
   Blob bl = blob_view(blob, H, I);
   for (int b = 0; b < B; ++b)
     swiglu_expert(
         H, I, x + (size_t)b * H, [&](int n, int k) { return mx_weight(bl.codes[0], bl.scales[0], H, n, k); },
         [&](int n, int k) { return mx_weight(bl.codes[1], bl.scales[1], H, n, k); },
-        [&](int m, int n) { return mx_weight(bl.codes[2], bl.scales[2], I, m, n); }, out + (size_t)b * H);
+        [&](int m, int n) { return mx_weight(bl.codes[2], bl.scales[2], I, m, n); }, out + (size_t)b * H,
+        mx8 != 0);
+}
+
+void oracle_routed_expert(const uint8_t* blob, int H, int I, const uint16_t* x, int B, float* out) {
+  oracle_routed_expert_ex(blob, H, I, x, B, out, 0);
 }
 
 // ---- whole layer --------------------------------------------------------------
@@ -246,10 +325,13 @@ void oracle_routed_expert(const uint8_t* blob, int H, int I, const uint16_t* x, 
 // may be NULL.  Optional outputs: logits [B][E], shared_out [B][H],
 // slot_out [B][k][H].  Returns -1 if a selected expert has no blob, else the
 // router's order-dependence count.
-int oracle_moe_layer(int H, int I, int E, int k, int Is, const uint16_t* router_w, const float* router_bias,
-                     const uint16_t* shared_gate, const uint16_t* shared_up, const uint16_t* shared_down,
-                     const uint8_t* const* experts, const uint16_t* x, const float* residual, int B, float* out,
-                     int32_t* idx, float* gate, float* logits_out, float* shared_out, float* slot_out) {
+// mx8 != 0: the routed experts run the FP4 x MXFP8 variant (their
+// activations quantised to MXFP8); the router and the bf16 shared expert are
+// unchanged.
+int oracle_moe_layer_ex(int H, int I, int E, int k, int Is, const uint16_t* router_w, const float* router_bias,
+                        const uint16_t* shared_gate, const uint16_t* shared_up, const uint16_t* shared_down,
+                        const uint8_t* const* experts, const uint16_t* x, const float* residual, int B, float* out,
+                        int32_t* idx, float* gate, float* logits_out, float* shared_out, float* slot_out, int mx8) {
   std::vector<float> logits((size_t)B * E);
   int od = oracle_router_logits(x, router_w, router_bias, B, H, E, logits.data());
   oracle_topk(logits.data(), B, E, k, idx, gate);
@@ -268,7 +350,7 @@ int oracle_moe_layer(int H, int I, int E, int k, int Is, const uint16_t* router_
     if (j == k) {
       if (Is > 0) oracle_shared_expert(shared_gate, shared_up, shared_down, H, Is, xb, 1, os.data() + (size_t)b * H);
     } else {
-      oracle_routed_expert(experts[idx[(size_t)b * k + j]], H, I, xb, 1, oj.data() + ((size_t)b * k + j) * H);
+      oracle_routed_expert_ex(experts[idx[(size_t)b * k + j]], H, I, xb, 1, oj.data() + ((size_t)b * k + j) * H, mx8);
     }
   }
   for (int b = 0; b < B; ++b) {
@@ -282,6 +364,14 @@ int oracle_moe_layer(int H, int I, int E, int k, int Is, const uint16_t* router_
     if (slot_out) std::memcpy(slot_out + (size_t)b * k * H, ob, sizeof(float) * (size_t)k * H);
   }
   return od;
+}
+
+int oracle_moe_layer(int H, int I, int E, int k, int Is, const uint16_t* router_w, const float* router_bias,
+                     const uint16_t* shared_gate, const uint16_t* shared_up, const uint16_t* shared_down,
+                     const uint8_t* const* experts, const uint16_t* x, const float* residual, int B, float* out,
+                     int32_t* idx, float* gate, float* logits_out, float* shared_out, float* slot_out) {
+  return oracle_moe_layer_ex(H, I, E, k, Is, router_w, router_bias, shared_gate, shared_up, shared_down, experts, x,
+                             residual, B, out, idx, gate, logits_out, shared_out, slot_out, 0);
 }
 
 // Host threads the layer's expert evaluations may use (OpenMP); the results
