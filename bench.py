@@ -70,7 +70,7 @@ def _pct(v, q):
     return float(np.percentile(np.asarray(v, np.float64), q))
 
 
-def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None):
+def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None, mxfp8=False):
     """Times `steps` layer steps launched back to back, then checks them.
 
     * timed pass: K steps enqueued back to back (one foreign call each);
@@ -84,6 +84,7 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None):
       overlapped its predecessor or took stale data would differ;
     * per-launch events: `event_reps` more launches, each bracketed by events
       recorded by the library, for the median / p10 / p90 of one launch.
+    mxfp8: time moe_decode_layer_mxfp8 (FP4 x MXFP8 routed experts) instead.
     """
     import numpy as np
     import torch
@@ -116,7 +117,7 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None):
             a, cs = _step_args(lib, layers[s % len(layers)], xs[s % variants], res[s], idx[s], gate[s], ws, stream)
             args.append(a)
             keep.append(cs)
-        call = lib.moe_decode_layer
+        call = lib.moe_decode_layer_mxfp8 if mxfp8 else lib.moe_decode_layer
         for s in range(warmup):
             assert call(*args[s]) == moe.MOE_OK
         torch.cuda.synchronize()
@@ -136,7 +137,8 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None):
             r_v = res0[s % variants].clone()
             i_v = torch.empty_like(idx[s])
             g_v = torch.empty_like(gate[s])
-            moe.moe_decode_layer(layers[s % len(layers)], xs[s % variants], r_v, idx=i_v, gate=g_v, ws=ws)
+            moe.moe_decode_layer(layers[s % len(layers)], xs[s % variants], r_v, idx=i_v, gate=g_v, ws=ws,
+                                 mxfp8=mxfp8)
             torch.cuda.synchronize()
             same = torch.equal(r_v.view(torch.int32), res[s].view(torch.int32)) and torch.equal(i_v, idx[s])
             mismatches += 0 if same else 1
@@ -146,8 +148,14 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None):
         for i in range(event_reps):
             s = warmup + i % steps
             r_e = res0[s % variants].clone()
-            moe.moe_decode_layer_timed(layers[s % len(layers)], xs[s % variants], r_e, idx[s], gate[s], ws, ev[i],
-                                       stream=stream)
+            if mxfp8:  # one kernel: events recorded around the call on the launch stream
+                ev[i][0].record(stream)
+                moe.moe_decode_layer(layers[s % len(layers)], xs[s % variants], r_e, idx=idx[s], gate=gate[s], ws=ws,
+                                     stream=stream, mxfp8=True)
+                ev[i][1].record(stream)
+            else:
+                moe.moe_decode_layer_timed(layers[s % len(layers)], xs[s % variants], r_e, idx[s], gate[s], ws,
+                                           ev[i], stream=stream)
         torch.cuda.synchronize()
     finally:
         for w, b in zip(layers, saved_bias):
@@ -432,8 +440,8 @@ def main():
     ap.add_argument("--variants", type=int, default=32, help="distinct input rows rotated across steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other batch sizes")
-    ap.add_argument("--extra", default="k3_b4,k3_b8,k3_b16,k3_b64_zipf",
-                    help="comma-separated other batch configurations to time")
+    ap.add_argument("--extra", default="k3_b4,k3_b8,k3_b16,k3_b64_zipf,k3_b8_mxfp8,k3_b64_zipf_mxfp8",
+                    help="comma-separated other batch configurations to time (_mxfp8: moe_decode_layer_mxfp8)")
     ap.add_argument("--no-stack", action="store_true", help="skip the 8-layer decode-step stack line")
     ap.add_argument("--no-probe", action="store_true", help="skip the stream-read ceiling and dense GEMV lines")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -466,11 +474,13 @@ def main():
         b8 = CONFIGS["k3_b8"]
         wanted = set(args.extra.split(","))
         for name, c in (("k3_b4", replace(b8, name="k3_b4", batch=4)), ("k3_b8", b8),
-                        ("k3_b16", replace(b8, name="k3_b16", batch=16)), ("k3_b64_zipf", CONFIGS["k3_b64_zipf"])):
+                        ("k3_b16", replace(b8, name="k3_b16", batch=16)), ("k3_b64_zipf", CONFIGS["k3_b64_zipf"]),
+                        ("k3_b8_mxfp8", b8), ("k3_b64_zipf_mxfp8", CONFIGS["k3_b64_zipf"])):
             if name not in wanted:
                 continue
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-            r = run_config(c, layers[:args.layers], max(20, args.steps // 2), args.warmup, args.variants)
+            r = run_config(c, layers[:args.layers], max(20, args.steps // 2), args.warmup, args.variants,
+                           mxfp8=name.endswith("_mxfp8"))
             extra[name] = {"batch": c.batch, "us_per_layer": round(r["us_per_layer"], 2),
                            "gbps": round(r["gbps"], 1), "frac_peak": round(r["gbps"] / PEAK_GBPS, 4),
                            "gpu_span_us_per_layer": round(r["gpu_span_us_per_layer"], 2),

@@ -237,6 +237,29 @@ moe_status moe_decode_layer(const moe_layer_weights* w, const uint16_t* x, float
                             int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_decode_layer_mxfp8 -- opt-in variant of moe_decode_layer whose routed
+ * experts multiply their FP4 weights by MXFP8 activations, the precision the
+ * expert kernel of "Kimi K3 on GB300: 13 kernels a layer, and what 842 and
+ * 423 tokens a second measure" uses (section "Why batch 1 on a rack is not
+ * only a bandwidth problem": FP4 x MXFP8 FC1/FC2 products).  The row entering
+ * a routed expert's FC1 and the SwiGLU output entering its FC2 are each
+ * quantised to MXFP8 (OCP Microscaling Formats v1.0: per block of 32
+ * consecutive elements an E8M0 scale 2^(floor(log2 amax) - 8), elements the
+ * nearest E4M3 value, ties to even, clamped to +-448) and the products run on
+ * gfx950's scaled FP4 x FP8 matrix instruction with the dot products summed
+ * in fp32.  The router, top-k, gates, the bf16 shared expert and the combine
+ * are exactly those of moe_decode_layer, so expert indices and gates are
+ * identical; the layer output differs from moe_decode_layer's by the
+ * activation quantisation (a few 1e-2 relative on the experts' part).
+ * Arguments, workspace and errors as moe_decode_layer; additionally
+ * MOE_ERR_UNSUPPORTED when 16 columns of the FC2 input (inter rounded up to
+ * 512, as E4M3 codes and scales) exceed 33,280 bytes of staging (inter above
+ * 1536).
+ */
+moe_status moe_decode_layer_mxfp8(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                                  int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_decode_layer_noalloc -- moe_decode_layer for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  It takes no workspace: the library's

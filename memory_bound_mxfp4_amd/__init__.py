@@ -26,7 +26,8 @@ EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size"
            "expert_gemv_mxfp4", "moe_decode_layer", "moe_decode_layer_kernel_count",
            "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "moe_pack_experts",
            "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "residual_add_rmsnorm_bf16",
-           "moe_workspace_status", "moe_stream_read_probe", "moe_decode_layer_noalloc", "moe_status_string")
+           "moe_workspace_status", "moe_stream_read_probe", "moe_decode_layer_noalloc", "moe_decode_layer_mxfp8",
+           "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,7 @@ def load():
         "residual_add_rmsnorm_bf16": (I, [P, P, I, I, F, P, P]),
         "moe_workspace_status": (I, [P, Z, P, P]),
         "moe_decode_layer_noalloc": (I, [P, P, P, I, P, P, P, P]),
+        "moe_decode_layer_mxfp8": (I, [P, P, P, I, P, P, P, Z, P]),
         "moe_stream_read_probe": (I, [P, Z, I, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
     }
@@ -250,8 +252,9 @@ def expert_gemv_mxfp4(codes, scales, x, n: int, k: int, y=None, stream=None):
     return y
 
 
-def moe_decode_layer(w: LayerWeights, x, residual, idx=None, gate=None, ws=None, stream=None):
-    """The whole layer; `residual` (fp32 [B][H]) is updated in place. Returns (idx, gate)."""
+def moe_decode_layer(w: LayerWeights, x, residual, idx=None, gate=None, ws=None, stream=None, mxfp8=False):
+    """The whole layer; `residual` (fp32 [B][H]) is updated in place. Returns (idx, gate).
+    mxfp8: the routed experts' FP4 x MXFP8 variant (moe_decode_layer_mxfp8)."""
     import torch
     B = x.shape[0]
     dev = x.device
@@ -259,8 +262,10 @@ def moe_decode_layer(w: LayerWeights, x, residual, idx=None, gate=None, ws=None,
     gate = torch.empty((B, w.top_k), dtype=torch.float32, device=dev) if gate is None else gate
     ws = alloc_workspace(w, B, dev) if ws is None else ws
     cs = w.c_struct()
-    _check(load().moe_decode_layer(ctypes.byref(cs), _ptr(x), _ptr(residual), B, _ptr(idx), _ptr(gate), _ptr(ws),
-                                   ws.numel(), _stream(stream)), "moe_decode_layer")
+    f, name = (load().moe_decode_layer_mxfp8, "moe_decode_layer_mxfp8") if mxfp8 else \
+        (load().moe_decode_layer, "moe_decode_layer")
+    _check(f(ctypes.byref(cs), _ptr(x), _ptr(residual), B, _ptr(idx), _ptr(gate), _ptr(ws), ws.numel(),
+             _stream(stream)), name)
     return idx, gate
 
 

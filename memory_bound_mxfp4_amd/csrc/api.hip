@@ -155,9 +155,10 @@ static const int kNumLayerKernels = 1;
 
 static moe_status run_layer(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
                             int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, hipStream_t s,
-                            void* const* events) {
+                            void* const* events, bool mx8 = false) {
   moe_status st = check_layer(w, batch);
   if (st != MOE_OK) return st;
+  if (mx8 && !mx8_supported(w->hidden, w->inter)) return MOE_ERR_UNSUPPORTED;
   if (!x || !residual || !topk_idx || !topk_gate || !ws) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(ws, 256)) return MOE_ERR_INVALID_ARGUMENT;
   if (w->expert_layout != MOE_EXPERTS_PACKED) return MOE_ERR_UNSUPPORTED;
@@ -185,7 +186,7 @@ static moe_status run_layer(const moe_layer_weights* w, const uint16_t* x, float
     return !events || hipEventRecord(static_cast<hipEvent_t>(events[ev++]), s) == hipSuccess;
   };
   if (!mark()) return MOE_ERR_HIP;
-  if (launch_layer(a, w->router_bias, w->router_w, topk_idx, s) != hipSuccess || !mark()) return MOE_ERR_HIP;
+  if (launch_layer(a, w->router_bias, w->router_w, topk_idx, s, mx8) != hipSuccess || !mark()) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
@@ -255,6 +256,12 @@ moe_status moe_decode_layer_noalloc(const moe_layer_weights* w, const uint16_t* 
                      hipMemcpyDeviceToDevice, s) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+moe_status moe_decode_layer_mxfp8(const moe_layer_weights* w, const uint16_t* x, float* residual, int batch,
+                                  int32_t* topk_idx, float* topk_gate, void* ws, size_t ws_bytes, void* stream) {
+  return run_layer(w, x, residual, batch, topk_idx, topk_gate, ws, ws_bytes, static_cast<hipStream_t>(stream),
+                   nullptr, true);
 }
 
 int moe_decode_layer_kernel_count(void) { return kNumLayerKernels; }

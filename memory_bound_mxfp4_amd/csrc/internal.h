@@ -83,7 +83,11 @@ struct LayerArgs {
   Workspace ws;
   float* residual;
 };
-hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* wr, int32_t* idx, hipStream_t s);
+// mx8: the routed experts' FP4 x MXFP8 variant (the matrix-core kernel at
+// every batch); mx8_supported: the shapes that variant covers.
+hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* wr, int32_t* idx, hipStream_t s,
+                        bool mx8 = false);
+bool mx8_supported(int H, int I);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_pack_experts(uint8_t* experts, int E, int H, int I, uint8_t* scratch, bool to_packed,
                                hipStream_t s);

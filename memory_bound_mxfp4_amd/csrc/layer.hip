@@ -48,6 +48,7 @@
 #include "moe_device.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 
@@ -178,7 +179,7 @@ __device__ __forceinline__ void cache_schedule(const LayerParams& p, WgState& st
   int* ro = sc + p.umax;
   int* rw = ro + p.umax + 1;
   int* cgo = rw + p.B * p.k;
-  if (p.B == 1) {
+  if (!OPQ) {  // the batch-1 kernel (the matrix-core kernel builds a schedule at every batch)
     if (TID_ < p.k) {
       uint64_t v[1];
       const int j = TID_;
@@ -1811,12 +1812,357 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
   }
 }
 
+// ---- FP4 x MXFP8 routed experts (opt-in: moe_decode_layer_mxfp8) ----------------
+//
+// The expert kernel of "Kimi K3 on GB300: 13 kernels a layer" (section "Why
+// batch 1 on a rack is not only a bandwidth problem") multiplies FP4 weights
+// by MXFP8 activations.  On gfx950 that product is one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per 16 rows x 128 elements x 16 columns,
+// which takes both operands as stored and their E8M0 block scales:
+//   A (FP4 weights): lane 16 q + r holds row r, elements 32 q .. 32 q + 31 of
+//     the 128-element step as 16 bytes -- exactly slab kb of a packed tile --
+//     and supplies the scale of (row r, block q): byte kb of the tile's scale
+//     dword, which the instruction's byte select picks;
+//   B (E4M3 activations): lane 16 q + r holds column r, elements 16 q ..
+//     16 q + 15 in its first 16 bytes and 64 + 16 q .. 64 + 16 q + 15 in its
+//     last 16, and supplies the scale of (column r, block q);
+//   D: lane 16 q + r holds rows 4 q .. 4 q + 3 of column r, as for the bf16
+//     instruction.
+// No FP4 decode runs on the vector ALU, and FC2 needs one product per step
+// instead of the bf16 path's hi + lo pair.  The activations are quantised to
+// MXFP8 inside the unit while they are staged: per block of 32 the E8M0 scale
+// 2^(floor(log2 amax) - 8) (8: the exponent of E4M3's largest power of two),
+// each element the nearest E4M3 value of v / scale, ties to even, magnitudes
+// past 448 clamped to 448 (OCP Microscaling Formats v1.0).
+// LDS of a unit: column c's codes at c * XQ (whole 512-element segments, zero
+// past K), then the scales: dword (c, s, q) holds in byte kb the scale of
+// block 16 s + 4 kb + q of column c (127, i.e. 1.0, past K).
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Nearest E4M3 code of v (ties to even), clamped to +-448; v finite.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a >= 464.0f) return s | 0x7Eu;  // past the largest finite value; 464 itself ties to 448 (the even code)
+  if (a < 0.015625f) return s | (uint32_t)__builtin_rintf(a * 512.0f);  // subnormals: multiples of 2^-9 (8: 2^-6)
+  uint32_t u = __float_as_uint(a);
+  u = (u + 0x7FFFFu + ((u >> 20) & 1u)) & 0xFFF00000u;  // significand to 3 bits, nearest even
+  return s | ((((u >> 23) - 120u) << 3) | ((u >> 20) & 7u));  // exponent bias 127 -> 7
+}
+
+// MXFP8 of one block of 32 values: the codes (byte j = element j) and the
+// E8M0 scale byte.
+__device__ __forceinline__ uint32_t mx8_block(const float (&v)[32], u32x4& c0, u32x4& c1) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  const int e = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));  // floor(log2 amax) - 8
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);      // 2^-e (e <= 119: a normal number)
+  uint32_t w[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+    w[d] = e4m3_code(v[4 * d] * inv) | (e4m3_code(v[4 * d + 1] * inv) << 8) | (e4m3_code(v[4 * d + 2] * inv) << 16) |
+           (e4m3_code(v[4 * d + 3] * inv) << 24);
+  c0 = u32x4{w[0], w[1], w[2], w[3]};
+  c1 = u32x4{w[4], w[5], w[6], w[7]};
+  return (uint32_t)(e + 127);
+}
+
+template <int KB>
+__device__ __forceinline__ f32x4 mfma_fp4_mx8(const u32x4& a, const u32x4& b0, const u32x4& b1, uint32_t sa,
+                                              uint32_t sb, f32x4 c) {
+  const i32x8 av{(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8 bv{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, KB, (int)sa, KB, (int)sb);
+}
+
+// Columns (a unit's rows of activations) and their MXFP8 staging: codes of
+// column c at c * xq, scale dwords at sc + ((c * S + s) * 4 + q) * 4.
+struct MxCols {
+  char* buf;
+  int xq;   // column stride of the codes (bytes)
+  int sc;   // byte offset of the scale dwords
+  int S;    // segments of 512 elements covered
+};
+
+// Stores the MXFP8 of block b (element 32 b ...) of column c; blocks past
+// the operand's K hold zero codes and scale 1.
+__device__ __forceinline__ void mx8_put(const MxCols& m, int c, int b, int seg0, u32x4 c0, u32x4 c1, uint32_t scale) {
+  char* col = m.buf + c * m.xq + 32 * (b - 16 * seg0);
+  *reinterpret_cast<u32x4*>(col) = c0;
+  *reinterpret_cast<u32x4*>(col + 16) = c1;
+  const int s = b / 16 - seg0, w = b % 16;
+  m.buf[m.sc + ((c * m.S + s) * 4 + (w & 3)) * 4 + (w >> 2)] = (char)scale;
+}
+
+// The 32 bf16 activations of block b of batch row `row` (zero past H).
+__device__ __forceinline__ void x_block(const LayerParams& p, int row, int b, float (&v)[32]) {
+  if (32 * b < p.H) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.x + (size_t)row * p.H + 32 * b);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 q = src[g];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v[8 * g + 2 * d] = bf16_lo(q[d]);
+        v[8 * g + 2 * d + 1] = bf16_hi(q[d]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+}
+
+// One 128-element step kb of segment s for a lane: its B fragment (column
+// col) and B scale dword.
+__device__ __forceinline__ void mx8_frag(const MxCols& m, int col, int s_local, int kb, int q, u32x4& b0, u32x4& b1,
+                                         uint32_t& sb) {
+  const char* base = m.buf + col * m.xq + 512 * s_local + 128 * kb + 16 * q;
+  b0 = *reinterpret_cast<const u32x4*>(base);
+  b1 = *reinterpret_cast<const u32x4*>(base + 64);
+  sb = *reinterpret_cast<const uint32_t*>(m.buf + m.sc + ((col * m.S + s_local) * 4 + q) * 4);
+}
+
+// A operand data and scale of one FP4 tile slab for a lane; on a partial
+// segment, blocks past the tile's SC are zeroed with scale 1.
+template <bool FULL>
+__device__ __forceinline__ void mx8_a(const u32x4& slab, uint32_t sv, int SC, int kb, int q, u32x4& a, uint32_t& sa) {
+  const bool ok = FULL || 4 * kb + q < SC;
+  a = ok ? slab : u32x4{0u, 0u, 0u, 0u};
+  sa = ok ? sv : 0x7F7F7F7Fu;
+}
+
+// FC1 + SwiGLU of rows [64 t, 64 t + 64) of routed expert a, column group cg,
+// with MXFP8 activations.  A narrow column group (all of K for every column
+// fits the staging region) quantises x once and streams with no barrier; a
+// wide one quantises segment by segment into two alternating buffers.
+template <bool FULL>
+__device__ __forceinline__ void mx_fc1_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg,
+                                            int t) {
+  const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
+  const int N = p.I, g = 4 * t + w;
+  const uint8_t* blob = p.experts + (size_t)st.s_active[a] * p.blob_bytes;
+  const int C1 = p.H / 32, S = (C1 + 15) / 16;
+  const int gl = min(g, (N + 15) / 16 - 1);
+  f32x4 ag{0.f, 0.f, 0.f, 0.f}, au{0.f, 0.f, 0.f, 0.f};
+  MfBuf ba, bb;
+  mf1_load<true, FULL>(p, blob, gl, 0, ba, 0.f);
+  if (S > 1) mf1_load<true, FULL>(p, blob, gl, 1, bb, 0.f);
+  load_cols(p, st, L, a, cg);
+  const int nc = L.nrows;
+  const bool live = r < nc;
+  const int col = live ? r : 0;
+  auto math = [&](const MxCols& m, int s, int s_local, const MfBuf& b) {
+    const int SC = FULL ? 16 : min(16, C1 - 16 * s);
+    auto step = [&](auto kbc) {
+      constexpr int kb = decltype(kbc)::value;
+      u32x4 b0, b1, ga, ua;
+      uint32_t sb, sg, su;
+      mx8_frag(m, col, s_local, kb, q, b0, b1, sb);
+      mx8_a<FULL>(b.q[0][kb], b.s[0], SC, kb, q, ga, sg);
+      mx8_a<FULL>(b.q[1][kb], b.s[1], SC, kb, q, ua, su);
+      ag = mfma_fp4_mx8<kb>(ga, b0, b1, sg, sb, ag);
+      au = mfma_fp4_mx8<kb>(ua, b0, b1, su, sb, au);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+  };
+  const int XQ = S * 512 + 16;
+  if (nc * (XQ + S * 16) <= MF_STAGE_BYTES) {
+    const MxCols m{mfb, XQ, nc * XQ, S};
+    for (int i = tidx(); i < nc * S * 16; i += 256) {
+      const int c = i / (S * 16), b = i - c * (S * 16);
+      float v[32];
+      x_block(p, L.slot[c] / p.k, b, v);
+      u32x4 c0, c1;
+      const uint32_t sc = mx8_block(v, c0, c1);
+      mx8_put(m, c, b, 0, c0, c1, 32 * b < p.H ? sc : 127u);
+    }
+    __syncthreads();
+    for (int s = 0; s < S; s += 2) {
+      math(m, s, s, ba);
+      if (s + 2 < S) mf1_load<true, FULL>(p, blob, gl, s + 2, ba, ag[0] + au[0]);
+      if (s + 1 < S) {
+        math(m, s + 1, s + 1, bb);
+        if (s + 3 < S) mf1_load<true, FULL>(p, blob, gl, s + 3, bb, ag[0] + au[0]);
+      }
+    }
+  } else {
+    // two buffers of one segment each: 16 columns x (512 + 16) code bytes, then 16 x 16 scale bytes
+    constexpr int XQS = 512 + 16, BUF = MF_COLS * XQS + MF_COLS * 16;
+    auto buf = [&](int s) { return MxCols{mfb + (s & 1) * BUF, XQS, MF_COLS * XQS, 1}; };
+    const int c_me = tidx() >> 4, j_me = tidx() & 15;  // this thread's (column, block) of a segment
+    auto quant_put = [&](int s, const float (&v)[32]) {
+      u32x4 c0, c1;
+      const uint32_t sc = mx8_block(v, c0, c1);
+      mx8_put(buf(s), c_me, 16 * s + j_me, s, c0, c1, 32 * (16 * s + j_me) < p.H ? sc : 127u);
+    };
+    {
+      float v[32];
+      x_block(p, c_me < nc ? L.slot[c_me] / p.k : 0, j_me, v);
+      if (c_me < nc) quant_put(0, v);
+    }
+    __syncthreads();
+    for (int s = 0; s < S; s += 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ss = s + h;
+        if (ss < S) {
+          float v[32];
+          if (ss + 1 < S) x_block(p, c_me < nc ? L.slot[c_me] / p.k : 0, 16 * (ss + 1) + j_me, v);
+          MfBuf& b = h ? bb : ba;
+          math(buf(ss), ss, 0, b);
+          if (ss + 2 < S) mf1_load<true, FULL>(p, blob, gl, ss + 2, b, ag[0] + au[0]);
+          if (ss + 1 < S && c_me < nc) quant_put(ss + 1, v);
+          __syncthreads();
+        }
+      }
+    }
+  }
+  // h = silu(gate) * up: rows 16 g + 4 q + i of column r, as fp32 (two 8-byte coherent stores)
+  float* hout = reinterpret_cast<float*>(p.hr_p);
+  const int n0 = 16 * g + 4 * q;
+  if (n0 < N && r < nc) {
+    float hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = silu_f(ag[i]) * au[i];
+    uint64_t* dst = reinterpret_cast<uint64_t*>(hout + (size_t)L.slot[r] * N + n0);
+    st_coh(dst, ((uint64_t)__float_as_uint(hv[1]) << 32) | __float_as_uint(hv[0]));
+    st_coh(dst + 1, ((uint64_t)__float_as_uint(hv[3]) << 32) | __float_as_uint(hv[2]));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every lane's h stores have completed
+  __syncthreads();
+  if (tidx() == 0) st_coh(hflag_at(p, a, cg, t), make_pair(1u, st.tag));
+}
+
+// FC2 of rows [512 t, 512 t + 512) of H of routed expert a, column group cg,
+// with the SwiGLU output quantised to MXFP8: all of K (I) for every column is
+// staged once (the envelope of the variant), then one pass per (128-row
+// tile, segment), one scaled MFMA per tile and step.
+template <bool FULL>
+__device__ __forceinline__ void mx_fc2_unit(const LayerParams& p, WgState& st, Lds& L, char* mfb, int a, int cg,
+                                            int t) {
+  const int nc = unit_ncols(p, st, a, cg);
+  const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
+  const int K = p.I, G = p.H / 16;
+  const uint8_t* down = p.experts + (size_t)st.s_active[a] * p.blob_bytes + (size_t)2 * p.I * (p.H / 32) * 17;
+  const int C2 = K / 32, S = (C2 + 15) / 16;
+  const int MT = min(MF_MT2, (G - 8 * MF_MT2 * t + 7) / 8);
+  auto groups = [&](int mt, int (&gt)[2]) {
+    gt[0] = min(8 * (MF_MT2 * t + mt) + w, G - 1);
+    gt[1] = min(8 * (MF_MT2 * t + mt) + w + 4, G - 1);
+  };
+  MfBuf ba, bb;
+  const int P = MT * S;
+  {
+    int gt[2];
+    groups(0, gt);
+    mf2_load<true, FULL>(p, down, gt, 0, ba, 0.f);
+    if (P > 1) {
+      groups(1 / S, gt);
+      mf2_load<true, FULL>(p, down, gt, 1 % S, bb, 0.f);
+    }
+  }
+  load_cols(p, st, L, a, cg);
+  {  // wait until every FC1 tile of this column group has published its h
+    const int ntile = (K + MF_NT1 - 1) / MF_NT1;
+    bool ok = true;
+    if (tidx() < ntile) {
+      uint64_t f[1];
+      const int ti = tidx();
+      ok = poll_pairs<1>(hflag_at(p, a, cg, 0), 1, [&](int) { return ti; }, st.tag, f, SPIN_LIMIT,
+                         p.ctrl + CTRL_ERR);
+    }
+    if (!ok) set_error(p);
+  }
+  const int XQ = S * 512 + 16;
+  const MxCols m{mfb, XQ, nc * XQ, S};
+  const float* hsrc = reinterpret_cast<const float*>(p.hr_p);
+  __syncthreads();
+  for (int i = tidx(); i < nc * S * 16; i += 256) {
+    const int c = i / (S * 16), b = i - c * (S * 16);
+    float v[32];
+    if (32 * b < K) {
+      const uint64_t* src = reinterpret_cast<const uint64_t*>(hsrc + (size_t)L.slot[c] * K + 32 * b);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint64_t pr = ld_coh(src + j);
+        v[2 * j] = __uint_as_float((uint32_t)pr);
+        v[2 * j + 1] = __uint_as_float((uint32_t)(pr >> 32));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = 0.0f;
+    }
+    u32x4 c0, c1;
+    const uint32_t sc = mx8_block(v, c0, c1);
+    mx8_put(m, c, b, 0, c0, c1, 32 * b < K ? sc : 127u);
+  }
+  __syncthreads();
+  const int col = r < nc ? r : 0;
+  const f32x4 zero4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2] = {zero4, zero4};
+  for (int pp = 0; pp < P; pp += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ps = pp + h;
+      if (ps < P) {
+        MfBuf& b = h ? bb : ba;
+        const int mt = ps / S, sg = ps - mt * S;
+        const int SC = FULL ? 16 : min(16, C2 - 16 * sg);
+        auto step = [&](auto kbc) {
+          constexpr int kb = decltype(kbc)::value;
+          u32x4 b0, b1;
+          uint32_t sb;
+          mx8_frag(m, col, sg, kb, q, b0, b1, sb);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            u32x4 av;
+            uint32_t sa;
+            mx8_a<FULL>(b.q[tt][kb], b.s[tt], SC, kb, q, av, sa);
+            acc[tt] = mfma_fp4_mx8<kb>(av, b0, b1, sa, sb, acc[tt]);
+          }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+        if (ps + 2 < P) {
+          int gt[2];
+          groups((ps + 2) / S, gt);
+          mf2_load<true, FULL>(p, down, gt, (ps + 2) % S, b, acc[0][0] + acc[1][0]);
+        }
+        if (sg == S - 1) {
+          if (r < nc) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const int gg = 8 * (MF_MT2 * t + mt) + w + 4 * tt;
+              if (gg < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  st_pair_f32(p.or_p + (size_t)L.slot[r] * p.H + 16 * gg + 4 * q + i, acc[tt][i], st.tag);
+              }
+            }
+          }
+          acc[0] = zero4;
+          acc[1] = zero4;
+        }
+      }
+    }
+  }
+}
+
 // ---- the kernel ------------------------------------------------------------------
 
 // FULL: the layer's shape makes every weight-stream segment and FC2 row group
 // complete (H % 7168 == 0, I % 1536 == 0, Is % 384 == 0), so the streams need
 // no clamping or masking.
-template <int RG, bool FULL, int TPL>
+template <int RG, bool FULL, int TPL, bool MX8>
 __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   extern __shared__ u32x4 lds_raw[];
   u32x4* xs = lds_raw;
@@ -1868,12 +2214,14 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
         const int NCG = st.s_cg_off[U];  // column groups of all active experts
         if (rel < NCG * p.mf_t1) {
           const int gc = rel / p.mf_t1, ae = find_expert(st, gc);
-          mf_fc1_unit<true, FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t1);
+          if constexpr (MX8) mx_fc1_unit<FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t1);
+          else mf_fc1_unit<true, FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t1);
         } else if ((rel -= NCG * p.mf_t1) < p.n_s2) {
           mf_fc2_unit<false, FULL>(p, st, L, mfb, -1, rel / p.mf_t2s, rel % p.mf_t2s);
         } else if ((rel -= p.n_s2) < NCG * p.mf_t2) {
           const int gc = rel / p.mf_t2, ae = find_expert(st, gc);
-          mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t2);
+          if constexpr (MX8) mx_fc2_unit<FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t2);
+          else mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t2);
         } else if ((rel -= NCG * p.mf_t2) < p.B * p.n_tile) {
           combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile);
         } else {
@@ -1924,19 +2272,21 @@ struct LaunchShape {
   int lds_h_off, lds_sched_off;
 };
 
-static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
+// mf: the matrix-core kernel (every batch > 1, and the FP4 x MXFP8 variant
+// at every batch); else the batch-1 kernel.
+static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B, bool mf) {
   LaunchShape s;
-  s.rg = (B == 1) ? 1 : 4;
+  s.rg = mf ? 4 : 1;
   // FULL: every packed tile holds 16 blocks (H, I multiples of 512), every
   // bf16 shared-expert stream segment is complete, and every unit's rows exist
   s.full = (H % 512 == 0) && (I % 512 == 0) && (H % (32 * 8 * CPL1) == 0) && (Is % (8 * 8 * CPL2) == 0) &&
            (Is % NTS1 == 0) && (H % NTR2 == 0) && (H % NTS2 == 0);
-  if (B > 1) s.full = (H % 512 == 0) && (I % 512 == 0);  // the MFMA path: every packed tile is complete
+  if (mf) s.full = (H % 512 == 0) && (I % 512 == 0);  // the MFMA path: every packed tile is complete
   s.xstride = ((H / 8 + 7) / 8) * 8;
   int K2 = I > Is ? I : Is;
   s.hstride = ((K2 / 4 + 7) / 8) * 8;  // fp32 h rows (shared expert FC2)
-  if (B == 1 && 2 * h_lo_offset(I) > s.hstride) s.hstride = 2 * h_lo_offset(I);  // bf16 hi + lo rows (routed FC2)
-  size_t x_bytes = B > 1 ? 0 : (size_t)s.rg * s.xstride * 16;  // batch > 1: no x rows in LDS
+  if (!mf && 2 * h_lo_offset(I) > s.hstride) s.hstride = 2 * h_lo_offset(I);  // bf16 hi + lo rows (routed FC2)
+  size_t x_bytes = mf ? 0 : (size_t)s.rg * s.xstride * 16;  // matrix-core kernel: no x rows in LDS
   // routing reuses this region: top-k survivors and slots, then the
   // schedule's counts (2E) and slot ids (B*k)
   size_t keys_bytes = (size_t)topk_lds_words(E <= 1024 ? 4 : 16) * 4, cnt_bytes = (size_t)(2 * E + B * k) * 4;
@@ -1945,19 +2295,19 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B) {
   // batch > 1: the MFMA staging buffers (two 16-column segments) alias this
   // region, and no h rows are staged
   const size_t mf_bytes = MF_STAGE_BYTES;
-  if (B > 1 && mf_bytes > xr) xr = mf_bytes;
+  if (mf && mf_bytes > xr) xr = mf_bytes;
   xr = align256(xr);
   s.lds_h_off = (int)xr;
-  size_t hr = B > 1 ? 0 : align256((size_t)s.rg * s.hstride * 16);
+  size_t hr = mf ? 0 : align256((size_t)s.rg * s.hstride * 16);
   s.lds_sched_off = (int)(xr + hr);
   const size_t slots = (size_t)B * k, umax = slots < (size_t)E ? slots : (size_t)E;
   s.lds = xr + hr + align256(4 * (3 * umax + 2 + slots));
   return s;
 }
 
-template <int RG, bool FULL, int TPL>
+template <int RG, bool FULL, int TPL, bool MX8 = false>
 static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
-  auto kern = k_moe_layer<RG, FULL, TPL>;
+  auto kern = k_moe_layer<RG, FULL, TPL, MX8>;
   static thread_local int cached[2] = {-1, -1};  // (lds bytes, blocks per CU)
   int per_cu = 0;
   if (cached[0] == (int)lds) {
@@ -1973,7 +2323,14 @@ static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* wr, int32_t* idx, hipStream_t s) {
+bool mx8_supported(int H, int I) {
+  // FC2 stages all of I for 16 columns at once (codes and scales)
+  const int S2 = (I / 32 + 15) / 16;
+  return MF_COLS * (S2 * 512 + 16 + S2 * 16) <= MF_STAGE_BYTES && H > 0;
+}
+
+hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* wr, int32_t* idx, hipStream_t s,
+                        bool mx8) {
   LayerParams p;
   p.H = a.H;
   p.I = a.I;
@@ -2005,14 +2362,15 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.or_p = a.ws.or_p;
   p.ctrl = a.ws.ctrl;
   p.umax = a.ws.umax;
-  const LaunchShape sh = launch_shape(a.H, a.I, a.E, a.k, a.Is, a.B);
+  const bool mf = a.B > 1 || mx8;
+  const LaunchShape sh = launch_shape(a.H, a.I, a.E, a.k, a.Is, a.B, mf);
   p.n_rt_e = (a.E + 3) / 4;  // router units per row block: 4 experts each
   p.xstride = sh.xstride;
   p.hstride = sh.hstride;
-  p.n_rb = a.B > 1 ? (a.B + 7) / 8 : 1;  // router row blocks: 8 rows (batch 1: one)
+  p.n_rb = mf ? (a.B + 7) / 8 : 1;  // router row blocks: 8 rows (batch-1 kernel: one)
   p.n_rt = p.n_rt_e * p.n_rb;
   p.n_ro = a.B;
-  p.n_sch = a.B > 1 ? 1 : 0;
+  p.n_sch = mf ? 1 : 0;
   p.n_s1 = a.Is > 0 ? (a.Is + NTS1 - 1) / NTS1 : 0;
   p.T1 = (a.I + NT1 - 1) / NT1;
   p.n_s2 = a.Is > 0 ? (a.H + NTS2 - 1) / NTS2 : 0;
@@ -2023,7 +2381,7 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.mf_t2 = (a.H + MF_NT2 - 1) / MF_NT2;
   p.mf_t2s = (a.H + 127) / 128;
   p.mf_cgs = (a.B + MF_COLS - 1) / MF_COLS;
-  if (a.B > 1) {  // MFMA path: shared expert units per column group
+  if (mf) {  // MFMA path: shared expert units per column group
     p.n_s1 = a.Is > 0 ? p.mf_cgs * p.mf_t1s : 0;
     p.n_s2 = a.Is > 0 ? p.mf_cgs * p.mf_t2s : 0;
   }
@@ -2034,6 +2392,10 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.lds_h_off = sh.lds_h_off;
   p.lds_sched_off = sh.lds_sched_off;
   // top-k keys per lane in the first selection phase: E <= 1024 -> 4, else 16
+  if (mx8) {
+    if (a.E <= 1024) return sh.full ? launch_t<4, true, 4, true>(p, sh.lds, s) : launch_t<4, false, 4, true>(p, sh.lds, s);
+    return sh.full ? launch_t<4, true, 16, true>(p, sh.lds, s) : launch_t<4, false, 16, true>(p, sh.lds, s);
+  }
   if (a.E <= 1024) {
     if (sh.rg == 1) return sh.full ? launch_t<1, true, 4>(p, sh.lds, s) : launch_t<1, false, 4>(p, sh.lds, s);
     return sh.full ? launch_t<4, true, 4>(p, sh.lds, s) : launch_t<4, false, 4>(p, sh.lds, s);
