@@ -70,9 +70,15 @@ def _pct(v, q):
     return float(np.percentile(np.asarray(v, np.float64), q))
 
 
-def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None, mxfp8=False):
+CLOCK_WARMUP_S = 0.3
+
+
+def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None, mxfp8=False,
+               clock_warmup_s=CLOCK_WARMUP_S):
     """Times `steps` layer steps launched back to back, then checks them.
 
+    * clock warm-up: `clock_warmup_s` seconds of untimed steps, then the W
+      warm-up steps;
     * timed pass: K steps enqueued back to back (one foreign call each);
       wall clock between two synchronisations, and two HIP events recorded on
       the launch stream before the first and after the last launch (the GPU
@@ -118,6 +124,22 @@ def run_config(cfg, layers, steps, warmup, variants, seed=0, event_reps=None, mx
             args.append(a)
             keep.append(cs)
         call = lib.moe_decode_layer_mxfp8 if mxfp8 else lib.moe_decode_layer
+        # Clock warm-up: after an idle spell the first ~100 launches run while
+        # the GPU clocks ramp up from their idle state (7-8% slower); untimed
+        # steps for `clock_warmup_s` bring them to their steady state first.
+        r_w = res0[0].clone()  # the warm-up steps' own residual (the timed steps' inputs stay untouched)
+        wargs = []
+        for j in range(len(layers)):
+            a, cs = _step_args(lib, layers[j], xs[j % variants], r_w, idx[0], gate[0], ws, stream)
+            wargs.append(a)
+            keep.append(cs)
+        t_w = time.perf_counter()
+        n_w = 0
+        while time.perf_counter() - t_w < clock_warmup_s:
+            assert call(*wargs[n_w % len(wargs)]) == moe.MOE_OK
+            n_w += 1
+            if n_w % 64 == 0:
+                torch.cuda.synchronize()
         for s in range(warmup):
             assert call(*args[s]) == moe.MOE_OK
         torch.cuda.synchronize()
@@ -404,6 +426,13 @@ def run_stack(stack, steps, warmup, graph=True, seed=0):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     idx = []
     with torch.cuda.stream(s):
+        t_w = time.perf_counter()  # clock warm-up (untimed), as for the single layer
+        while time.perf_counter() - t_w < CLOCK_WARMUP_S:
+            if g is not None:
+                g.replay()
+            else:
+                stack.step(h, stream=s)
+            s.synchronize()
         e0.record(s)
         for _ in range(steps):
             if g is not None:
@@ -535,6 +564,7 @@ def main():
         "kernels_per_layer": len(main_r["launch_us"]),
         "validated": main_r["validated"],
         "gpu_span_us_per_layer": round(k_us, 2),
+        "clock_warmup_s": CLOCK_WARMUP_S,
         "launch_us_events": main_r["launch_us"],
         "roofline": {"kernel": "k_moe_layer", "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": recorded_traffic(),
