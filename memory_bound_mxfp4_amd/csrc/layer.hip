@@ -72,6 +72,7 @@ constexpr int CPL1 = 7;   // FC1: 16-byte chunks per lane per pass (half-wave ro
 constexpr int CPL2 = 6;   // FC2: 16-byte chunks per lane per pass (8 lanes per row)
 constexpr int MAX_ROWS = MOE_MAX_BATCH;    // activation rows one expert can have
 constexpr unsigned SPIN_LIMIT = 1u << 20;  // ~1 s of polls (at ~1 us each) before a wait gives up
+constexpr int RT_F64_MIN_BATCH = 16;       // batches above this run the router on the fp64 matrix cores
 
 struct LayerParams {
   int H, I, E, k, Is, B;
@@ -100,7 +101,8 @@ struct LayerParams {
   uint64_t* or_p;
   unsigned* ctrl;
   int umax;
-  int n_rt_e;    // router units per row block (4 experts a unit)
+  int rt_f64;    // batch > 16: router units on the matrix cores (16 experts x 16 rows)
+  int n_rt_e;    // router units per row block (4 experts a unit; 16 on the matrix cores)
   int n_rb;      // router row blocks
   int n_rt;      // router units = n_rt_e * n_rb
   int n_ro;      // routing units (one per row)
@@ -1015,6 +1017,67 @@ __device__ __forceinline__ void router_mf_unit(const LayerParams& p, WgState& st
       const double t = ((part[i] + part[32 + i]) + part[64 + i]) + part[96 + i];
       st_pair_f32(p.logits_p + (size_t)(b0 + r) * p.E + e, (float)(t + bb), st.tag);
     }
+  }
+}
+
+// Router unit on the matrix cores (batch > 16): experts 16 et .. 16 et + 15
+// against activation rows 16 rt .. 16 rt + 15, one v_mfma_f64_16x16x4_f64 per
+// 4 elements of K, the four waves splitting K.  Per step lane 16 q + r holds
+// the 8-element granule 4 j + q of expert row r (A) and of activation row r
+// (B), and 8 MFMAs take element i of it as k-slot q.  bf16 values and their
+// products are exact in fp64 and every partial sum is exact, so the logits
+// are the same exact sums, rounded once, as the other router units'; one
+// conversion per operand element instead of one per product, and the sums
+// run on the matrix pipe.  Eight 4-granule chunks per wave stay in flight;
+// the waves' partial tiles meet in LDS.  The result tile: element i of lane
+// 16 q + r is expert row 4 i + q, activation column r.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void router_f64_unit(const LayerParams& p, WgState& st, char* mfb, int u) {
+  constexpr int D = 8;  // chunks in flight per wave
+  const int et = u % p.n_rt_e, rt = u / p.n_rt_e;
+  const int w = tidx() >> 6, lane = tidx() & 63, r = lane & 15, q = lane >> 4;
+  const int e0 = 16 * et, b0 = 16 * rt;
+  const int C = p.H / 8, NCH = (C + 3) / 4, per = (NCH + 3) / 4;
+  const int ch0 = w * per, ch1 = min(NCH, ch0 + per);
+  const u32x4* wrow = reinterpret_cast<const u32x4*>(p.wr + (size_t)min(e0 + r, p.E - 1) * p.H);
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(p.x + (size_t)min(b0 + r, p.B - 1) * p.H);
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  u32x4 wb[D], xb[D];
+  auto gran = [&](int ch) { return min(4 * min(ch, NCH - 1) + q, C - 1); };
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    wb[i] = ld_weight16(wrow + gran(ch0 + i));
+    xb[i] = xrow[gran(ch0 + i)];
+  }
+  for (int j0 = ch0; j0 < ch1; j0 += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int ch = j0 + i;
+      const bool live = ch < ch1 && 4 * ch + q < C;
+      const uint32_t msk = live ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t wv = wb[i][d] & msk, xv = xb[i][d];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_lo(wv), (double)bf16_lo(xv), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)bf16_hi(wv), (double)bf16_hi(xv), acc, 0, 0, 0);
+      }
+      if (j0 + D + i < ch1) {  // refill this slot with the chunk D ahead
+        const int g = gran(j0 + D + i) + after(0, (float)acc[0]);
+        wb[i] = ld_weight16(wrow + g);
+        xb[i] = xrow[g];
+      }
+    }
+  }
+  double* part = reinterpret_cast<double*>(mfb);  // [4 waves][16 expert rows][16 columns]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[(w * 16 + 4 * i + q) * 16 + r] = acc[i];
+  __syncthreads();
+  const int t = tidx(), row = t >> 4, col = t & 15, e = e0 + row, b = b0 + col;
+  if (e < p.E && b < p.B) {
+    const double sum = ((part[t] + part[256 + t]) + part[512 + t]) + part[768 + t];
+    const double bb = p.bias ? (double)p.bias[e] : 0.0;
+    st_pair_f32(p.logits_p + (size_t)b * p.E + e, (float)(sum + bb), st.tag);
   }
 }
 
@@ -2192,8 +2255,12 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int rel = u;
     if (rel < p.n_rt) {
-      if constexpr (MF) router_mf_unit(p, st, L, rel);
-      else router_unit(p, st, rel);
+      if constexpr (MF) {
+        if (p.rt_f64) router_f64_unit(p, st, mfb, rel);
+        else router_mf_unit(p, st, L, rel);
+      } else {
+        router_unit(p, st, rel);
+      }
     } else if ((rel -= p.n_rt) < p.n_ro) {
       routing_unit<TPL>(p, st, L, reinterpret_cast<int*>(xs), rel);
     } else if ((rel -= p.n_ro) < p.n_sch) {
@@ -2364,10 +2431,11 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.umax = a.ws.umax;
   const bool mf = a.B > 1 || mx8;
   const LaunchShape sh = launch_shape(a.H, a.I, a.E, a.k, a.Is, a.B, mf);
-  p.n_rt_e = (a.E + 3) / 4;  // router units per row block: 4 experts each
+  p.rt_f64 = a.B > RT_F64_MIN_BATCH;
+  p.n_rt_e = p.rt_f64 ? (a.E + 15) / 16 : (a.E + 3) / 4;  // router units per row block: 16 or 4 experts each
   p.xstride = sh.xstride;
   p.hstride = sh.hstride;
-  p.n_rb = mf ? (a.B + 7) / 8 : 1;  // router row blocks: 8 rows (batch-1 kernel: one)
+  p.n_rb = p.rt_f64 ? (a.B + 15) / 16 : (mf ? (a.B + 7) / 8 : 1);  // row blocks: 16 rows, 8 rows, or the one row
   p.n_rt = p.n_rt_e * p.n_rb;
   p.n_ro = a.B;
   p.n_sch = mf ? 1 : 0;

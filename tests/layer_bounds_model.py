@@ -30,6 +30,7 @@ MF_NT2 = 128 * MF_MT2
 MF_XS_FP4 = 512 * 2 + 16
 MF_STAGE_BYTES = 2 * MF_COLS * MF_XS_FP4
 CTRL_WORDS = 4 * 32
+RT_F64_MIN_BATCH = 16
 
 
 def align256(n):
@@ -148,6 +149,7 @@ class Params:
     mf_t2: int = 0
     mf_t2s: int = 0
     mf_cgs: int = 0
+    rt_f64: bool = False
 
 
 def params(sh: Shape) -> Params:
@@ -155,8 +157,9 @@ def params(sh: Shape) -> Params:
     _, umax, tiles = ws_regions(sh)
     p = Params(sh, launch_shape(sh), umax, tiles)
     H, I, E, k, Is, B = sh.H, sh.I, sh.E, sh.k, sh.Is, sh.B
-    p.n_rt_e = (E + 3) // 4
-    p.n_rb = (B + 7) // 8 if B > 1 else 1
+    p.rt_f64 = B > RT_F64_MIN_BATCH
+    p.n_rt_e = (E + 15) // 16 if p.rt_f64 else (E + 3) // 4
+    p.n_rb = (B + 15) // 16 if p.rt_f64 else ((B + 7) // 8 if B > 1 else 1)
     p.n_rt = p.n_rt_e * p.n_rb
     p.n_ro = B
     p.n_sch = 1 if B > 1 else 0
@@ -280,6 +283,30 @@ def check_call(sh: Shape, idx: List[List[int]], bias: bool = False) -> int:
                     if bias:
                         chk("bias", 4 * e, 4)
                     chk("logits_p", 8 * e, 8)
+        elif p.rt_f64:  # router_f64_unit
+            et, rt = u % p.n_rt_e, u // p.n_rt_e
+            e0, b0 = 16 * et, 16 * rt
+            C = H // 8
+            NCH = (C + 3) // 4
+            per = (NCH + 3) // 4
+            for t, w, lane in _lanes():
+                r, q = lane & 15, lane >> 4
+                ch0, ch1 = w * per, min(NCH, w * per + per)
+                gran = lambda ch: min(4 * min(ch, NCH - 1) + q, C - 1)
+                chunks = list(range(ch0, ch0 + 8)) + list(range(ch0 + 8, ch1))
+                for ch in chunks:
+                    g = gran(ch)
+                    chk("wr", 2 * (min(e0 + r, E - 1) * H + 8 * g), 16)
+                    chk("x", 2 * (min(b0 + r, B - 1) * H + 8 * g), 16)
+                for i in range(4):
+                    chk("lds", 8 * ((w * 16 + 4 * i + q) * 16 + r), 8)
+                row, col = t >> 4, t & 15
+                for ww in range(4):
+                    chk("lds", 8 * (256 * ww + t), 8)
+                if e0 + row < E and b0 + col < B:
+                    if bias:
+                        chk("bias", 4 * (e0 + row), 4)
+                    chk("logits_p", 8 * ((b0 + col) * E + e0 + row), 8)
         else:
             eg, rb = u % p.n_rt_e, u // p.n_rt_e
             e0, b0 = 4 * eg, 8 * rb
