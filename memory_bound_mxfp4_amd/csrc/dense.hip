@@ -186,9 +186,99 @@ __global__ __launch_bounds__(128) void k_dense_gemv1(const uint16_t* __restrict_
   if (lane == 0 && n < N) y[n] = f32_to_bf16(acc);
 }
 
+// Batches of 2..64 rows on the matrix cores: a workgroup takes 16 weight
+// rows and every activation row at once (NCG groups of 16 columns), so each
+// weight is read once per call instead of once per few rows.  One
+// v_mfma_f32_16x16x32_bf16 per 32 elements and column group: lane 16 q + r
+// supplies 8 elements of weight row r (A) and of activation row 16 cg + r
+// (B); the four waves split K into 128-element segments (w, w + 4, ...), two
+// segments of weights in flight per wave, activations read from L2; the
+// partial sums meet in LDS and are rounded once to bf16.
+template <int NCG>
+__global__ __launch_bounds__(256) void k_dense_gemv_mf(const uint16_t* __restrict__ w, int N, int K,
+                                                       const uint16_t* __restrict__ x, int B,
+                                                       uint16_t* __restrict__ y) {
+  __shared__ float red[4][NCG][16][16];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int S = (K + 127) / 128;
+  const int P = wv < S ? (S - wv + 3) / 4 : 0;
+  const uint16_t* wrow = w + (size_t)min(n0 + r, N - 1) * K;
+  const uint16_t* xrow[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) xrow[cg] = x + (size_t)min(16 * cg + r, B - 1) * K;
+  const u32x4 z{0u, 0u, 0u, 0u};
+  f32x4 acc[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) acc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // XP: activation column groups fetched with the weights (the rest are read
+  // in the math, from L2)
+  constexpr int XP = NCG <= 2 ? NCG : 0;
+  struct Buf {
+    u32x4 w[4];
+    u32x4 x[XP > 0 ? XP : 1][4];
+  };
+  Buf ba, bb;
+  auto load = [&](Buf& b, int pp) {
+    const int s = wv + 4 * pp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = min(s * 128 + 32 * j + 8 * q, K - 8);
+      b.w[j] = ld_weight16(wrow + k0);
+#pragma unroll
+      for (int cg = 0; cg < XP; ++cg) b.x[cg][j] = ld16(xrow[cg] + k0);
+    }
+  };
+  auto math = [&](const Buf& b, int pp) {
+    const int s = wv + 4 * pp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = s * 128 + 32 * j + 8 * q;
+      const bool ok = k0 < K;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, ok ? b.w[j] : z);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        const u32x4 xv = ok ? (cg < XP ? b.x[cg < XP ? cg : 0][j] : ld16(xrow[cg] + k0)) : z;
+        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, xv), acc[cg], 0, 0, 0);
+      }
+    }
+  };
+  if (P > 0) load(ba, 0);
+  if (P > 1) load(bb, 1);
+  for (int pp = 0; pp < P; pp += 2) {
+    math(ba, pp);
+    if (pp + 2 < P) load(ba, pp + 2);
+    if (pp + 1 < P) {
+      math(bb, pp + 1);
+      if (pp + 3 < P) load(bb, pp + 3);
+    }
+  }
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wv][cg][4 * q + i][r] = acc[cg][i];
+  __syncthreads();
+  const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const float v = ((red[0][cg][row][col] + red[1][cg][row][col]) + red[2][cg][row][col]) + red[3][cg][row][col];
+    const int n = n0 + row, b = 16 * cg + col;
+    if (n < N && b < B) y[(size_t)b * N + n] = f32_to_bf16(v);
+  }
+}
+
 hipError_t launch_dense_gemv(const uint16_t* w, int N, int K, const uint16_t* x, int B, uint16_t* y, hipStream_t s) {
   if (B == 1 && reinterpret_cast<uintptr_t>(x) % 16 == 0) {
     hipLaunchKernelGGL(k_dense_gemv1, dim3((N + 1) / 2), dim3(128), 0, s, w, N, K, x, y);
+    return hipGetLastError();
+  }
+  if (B > 1 && reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0) {
+    const dim3 grid((N + 15) / 16), block(256);
+    const int ncg = (B + 15) / 16;
+    if (ncg == 1) hipLaunchKernelGGL(k_dense_gemv_mf<1>, grid, block, 0, s, w, N, K, x, B, y);
+    else if (ncg == 2) hipLaunchKernelGGL(k_dense_gemv_mf<2>, grid, block, 0, s, w, N, K, x, B, y);
+    else if (ncg == 3) hipLaunchKernelGGL(k_dense_gemv_mf<3>, grid, block, 0, s, w, N, K, x, B, y);
+    else hipLaunchKernelGGL(k_dense_gemv_mf<4>, grid, block, 0, s, w, N, K, x, B, y);
     return hipGetLastError();
   }
   size_t row_bytes = (size_t)K * 2;

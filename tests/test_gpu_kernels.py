@@ -113,3 +113,19 @@ def test_dense_pieces_match_oracle():
     assert np.array_equal(h2.cpu().numpy(), ref)
     x1 = moe.rmsnorm_bf16(hh, 1e-6)
     assert torch.equal(x1, x2)
+
+
+@pytest.mark.parametrize("B", [1, 2, 8, 17, 64])
+@pytest.mark.parametrize("N,K", [(512, 7168), (100, 520)])
+def test_dense_gemv_batches_match_oracle(B, N, K):
+    """dense_gemv_bf16 at every batch shape (one row on the vector ALU, 2..64
+    rows on the matrix cores; ragged N and K): each output within one bf16
+    ulp of the oracle's rounding of the exact sum, and nearly always equal."""
+    import torch
+    print(f"[case] dense gemv B{B} N{N} K{K}", flush=True)
+    w = synth.fill_bf16(3, synth.tag(0, synth.KIND_DENSE, 0, 1), 0.02, N * K).reshape(N, K)
+    x = synth.fill_bf16(3, synth.tag(0, synth.KIND_X, 0, B), 1.0, B * K).reshape(B, K)
+    y_ref = oracle.dense_gemv_bf16(w, x)
+    y = moe.dense_gemv_bf16(_dev(w), _dev(x)).view(torch.int16).cpu().numpy().view(np.uint16)
+    dy = np.abs(y.astype(np.int32) - y_ref.astype(np.int32))
+    assert dy.max() <= 1 and (dy > 0).mean() < 0.01, (int(dy.max()), float((dy > 0).mean()))
