@@ -473,6 +473,8 @@ def main():
                     help="comma-separated other batch configurations to time (_mxfp8: moe_decode_layer_mxfp8)")
     ap.add_argument("--no-stack", action="store_true", help="skip the 8-layer decode-step stack line")
     ap.add_argument("--no-probe", action="store_true", help="skip the stream-read ceiling and dense GEMV lines")
+    ap.add_argument("--stack-prefetch", default="none",
+                    help="comma-separated side-stream prefetch modes of the stack to time (none, dense, moe, both)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the scaled HBM traffic of k_moe_layer from two counter CSVs and exit")
     args = ap.parse_args()
@@ -520,13 +522,16 @@ def main():
         sc = stack_cfg()
         print("[bench] timing the 8-layer decode-step stack", file=sys.stderr, flush=True)
         dense = [dense_device(sc, 0, l) for l in range(sc.layers)]
-        stack = DecodeStack(layers[:sc.layers], dense, sc.batch, sc.rms_eps)
-        r = run_stack(stack, max(5, args.steps // 6), 2)
-        extra["k3_stack8"] = {"batch": sc.batch, "layers": sc.layers, "us_per_step": round(r["us_per_step"], 1),
-                              "us_per_layer": round(r["us_per_layer"], 2), "gbps": round(r["gbps"], 1),
-                              "frac_peak": round(r["gbps"] / PEAK_GBPS, 4), "bytes_per_step": r["bytes_per_step"],
-                              "hip_graph": r["graph"], "kernels_per_step": r["kernels_per_step"]}
-        del stack, dense
+        for mode in args.stack_prefetch.split(","):
+            stack = DecodeStack(layers[:sc.layers], dense, sc.batch, sc.rms_eps, prefetch=mode)
+            r = run_stack(stack, max(5, args.steps // 6), 2)
+            key = "k3_stack8" if mode == "none" else f"k3_stack8_prefetch_{mode}"
+            extra[key] = {"batch": sc.batch, "layers": sc.layers, "us_per_step": round(r["us_per_step"], 1),
+                          "us_per_layer": round(r["us_per_layer"], 2), "gbps": round(r["gbps"], 1),
+                          "frac_peak": round(r["gbps"] / PEAK_GBPS, 4), "bytes_per_step": r["bytes_per_step"],
+                          "hip_graph": r["graph"], "kernels_per_step": r["kernels_per_step"], "prefetch": mode}
+            del stack
+        del dense
     probe = dense = None
     if not args.no_probe:
         del layers

@@ -334,6 +334,29 @@ moe_status residual_add_rmsnorm_bf16(float* h, const uint16_t* t, int batch, int
  */
 moe_status moe_stream_read_probe(const void* buf, size_t bytes, int blocks_per_cu, uint32_t* sink, void* stream);
 
+/*
+ * moe_prefetch -- read a table of weight ranges once with ordinary
+ * (allocating) loads, so that they sit in the device's memory-side
+ * last-level cache (256 MB on MI355X) when a later kernel streams them: the
+ * "prefetch on a third stream" of "Kimi K3 on GB300: 13 kernels a layer"
+ * (section "What the fused path changes"), where a small kernel walks a
+ * table of upcoming weight ranges.  Meant for a side stream, beside kernels
+ * that leave HBM idle (norms, launch gaps); it writes nothing and its
+ * results are not needed by anyone, so nothing has to wait for it.
+ *   ranges   host array of n_ranges (1..MOE_PREFETCH_MAX_RANGES) device
+ *            ranges, each 16-byte aligned with a size multiple of 16; the
+ *            table is copied into the launch, so it need not outlive the call
+ *   blocks   256-thread workgroups of the kernel (1..65536): how much of the
+ *            device it occupies beside the other stream's work
+ * Safe under stream capture (one kernel node, arguments by value).
+ */
+#define MOE_PREFETCH_MAX_RANGES 8
+typedef struct {
+  const void* ptr;
+  size_t bytes;
+} moe_range;
+moe_status moe_prefetch(const moe_range* ranges, int n_ranges, int blocks, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -27,7 +27,7 @@ EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size"
            "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "moe_pack_experts",
            "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "residual_add_rmsnorm_bf16",
            "moe_workspace_status", "moe_stream_read_probe", "moe_decode_layer_noalloc", "moe_decode_layer_mxfp8",
-           "moe_status_string")
+           "moe_prefetch", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -77,6 +77,7 @@ def load():
         "moe_workspace_status": (I, [P, Z, P, P]),
         "moe_decode_layer_noalloc": (I, [P, P, P, I, P, P, P, P]),
         "moe_decode_layer_mxfp8": (I, [P, P, P, I, P, P, P, Z, P]),
+        "moe_prefetch": (I, [P, I, I, P]),
         "moe_stream_read_probe": (I, [P, Z, I, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
     }
@@ -301,6 +302,20 @@ def moe_decode_layer_timed(w: LayerWeights, x, residual, idx, gate, ws, events, 
                                          _ptr(ws), ws.numel(), _stream(stream), arr, len(events)),
            "moe_decode_layer_timed")
     return idx, gate
+
+
+class RangeC(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("bytes", ctypes.c_size_t)]
+
+
+PREFETCH_MAX_RANGES = 8
+
+
+def prefetch(tensors, blocks: int = 256, stream=None):
+    """Read device tensors once into the last-level cache (moe_prefetch)."""
+    tensors = [t for t in tensors if t is not None]
+    arr = (RangeC * len(tensors))(*[RangeC(t.data_ptr(), t.numel() * t.element_size()) for t in tensors])
+    _check(load().moe_prefetch(arr, len(tensors), blocks, _stream(stream)), "moe_prefetch")
 
 
 def rmsnorm_bf16(h, eps: float = 1e-6, out=None, stream=None):

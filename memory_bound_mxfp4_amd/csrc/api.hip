@@ -327,6 +327,15 @@ moe_status moe_stream_read_probe(const void* buf, size_t bytes, int blocks_per_c
   return MOE_OK;
 }
 
+moe_status moe_prefetch(const moe_range* ranges, int n_ranges, int blocks, void* stream) {
+  if (!ranges || n_ranges < 1 || n_ranges > MOE_PREFETCH_MAX_RANGES || blocks < 1 || blocks > 65536)
+    return MOE_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < n_ranges; ++i)
+    if (!ranges[i].ptr || !aligned(ranges[i].ptr, 16) || ranges[i].bytes % 16) return MOE_ERR_INVALID_ARGUMENT;
+  if (launch_prefetch(ranges, n_ranges, blocks, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 moe_status rmsnorm_bf16(const float* in, int batch, int hidden, float eps, uint16_t* out, void* stream) {
   if (!in || !out || batch < 1 || batch > MOE_MAX_BATCH || hidden < 1 || !(eps >= 0.0f))
     return MOE_ERR_INVALID_ARGUMENT;

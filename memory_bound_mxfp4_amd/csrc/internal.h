@@ -102,6 +102,7 @@ hipError_t launch_residual_add_rmsnorm(float* h, const uint16_t* t, int B, int H
                                        hipStream_t s);
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, int blocks_per_cu, uint32_t* sink, hipStream_t s);
+hipError_t launch_prefetch(const moe_range* ranges, int n, int blocks, hipStream_t s);
 
 int num_cus();
 

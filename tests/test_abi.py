@@ -140,3 +140,13 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.moe_stream_read_probe(P(0x1000), 1 << 20, 0, P(0x3000), None) == -1
     assert lib.moe_stream_read_probe(P(0x1000), 1 << 20, 33, P(0x3000), None) == -1
     assert lib.moe_stream_read_probe(P(0x1000), 1 << 20, 4, None, None) == -1
+    # prefetch: no table, empty or oversized table, unaligned or ragged range, block count
+    R = moe.RangeC
+    ok = (R * 1)(R(0x1000, 4096))
+    assert lib.moe_prefetch(None, 1, 64, None) == -1
+    assert lib.moe_prefetch(ok, 0, 64, None) == -1
+    assert lib.moe_prefetch((R * 9)(*[R(0x1000, 4096)] * 9), 9, 64, None) == -1
+    assert lib.moe_prefetch((R * 1)(R(0x1008, 4096)), 1, 64, None) == -1
+    assert lib.moe_prefetch((R * 1)(R(0x1000, 4100)), 1, 64, None) == -1
+    assert lib.moe_prefetch((R * 1)(R(None, 4096)), 1, 64, None) == -1
+    assert lib.moe_prefetch(ok, 1, 0, None) == -1

@@ -106,3 +106,37 @@ def test_stack_graph_replay_matches_eager(k3_stack):
         torch.cuda.synchronize()
         assert np.array_equal(hg.cpu().numpy().view(np.uint32), eager.view(np.uint32)), rep
         assert np.array_equal(k3_stack.idx.cpu().numpy(), eager_idx), rep
+
+
+def test_stack_with_side_stream_prefetch_matches(k3_stack):
+    """The side-stream prefetch only reads: a step with it (eager and as a
+    replayed HIP graph) equals the plain step bit for bit."""
+    import torch
+    from memory_bound_mxfp4_amd.stack import DecodeStack
+    cfg = CONFIGS["k3_stack8"]
+    print("[case] stack with side-stream prefetch vs plain", flush=True)
+    h0 = torch.from_numpy(h0_host(cfg, 0)).cuda()
+    ref = h0.clone()
+    k3_stack.step(ref)
+    torch.cuda.synchronize()
+    pf = DecodeStack(k3_stack.layers, k3_stack.dense, cfg.batch, cfg.rms_eps, prefetch="both")
+    h = h0.clone()
+    pf.step(h)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int32), ref.view(torch.int32))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    hg = h0.clone()
+    with torch.cuda.stream(s):
+        pf.step(hg, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pf.step(hg, stream=s)
+    for rep in range(3):
+        hg.copy_(h0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hg.view(torch.int32), ref.view(torch.int32)), rep
