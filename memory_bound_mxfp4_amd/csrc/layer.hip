@@ -136,6 +136,7 @@ struct Lds {  // static LDS of the kernel
   int nxt[2];      // next unit index, alternating between iterations of the unit loop
   int U;           // distinct experts (once known)
   int sched_ok;    // batch > 1: the schedule's ready word arrived
+  uint64_t pre;    // batch 1: (unit-loop iteration + 1, next unit) posted mid-unit by thread 0
   int wtot[12];    // scan scratch
   int nrows;       // rows of the current unit
   float gates[MOE_MAX_TOPK];  // combine: gates of the current row
@@ -632,16 +633,14 @@ struct Fc1Tile {
     const int q = (threadIdx.x & 63) >> 4, c = 4 * (i >> 2) + q;
     return swz((16 * s + (FULL ? c : min(c, SC - 1))) * 4 + (i & 3));
   }
-  // The x granules are read one slab ahead; slab kb of both tiles is
-  // refilled with pass p + 2 as soon as its last dword is decoded, the scale
-  // vectors after the last slab.
-  __device__ void math(TileBuf1& b, int p, bool refill) {
+  // The x granules are read one slab ahead; with `refill`, slab kb of both
+  // tiles is refilled from the gate/up tile pair at gt2 (SC2 blocks: a pass
+  // two ahead, of this unit or of the next) as soon as its last dword is
+  // decoded, the scale vectors after the last slab.
+  __device__ void math(TileBuf1& b, int p, bool refill, const uint8_t* gt2, int SC2) {
     const int s = seg(p);
     const int q = (threadIdx.x & 63) >> 4;
     const int SC = FULL ? 16 : min(16, C1 - 16 * s);
-    const int s2 = seg(p + 2);
-    const int SC2 = FULL ? 16 : min(16, C1 - 16 * s2);
-    const uint8_t* gt2 = blob + 2 * tile_off(g, refill ? s2 : s, C1);
     u32x4 xv[4], xn[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) xv[d] = xs[xg(s, SC, d)];
@@ -1126,61 +1125,158 @@ __device__ __forceinline__ void shared_fc1_unit(const LayerParams& p, WgState& s
     f.nr = nr;
     for (int r = 0; r < RG; ++r) f.acc[r] = 0.0f;
     f.out = p.hs_p;
-    f.tag = st.tag;
     f.out_ld = p.Is;
     f.row = L.slot + g0;
     const int nrows = f.n0 < n_end ? (n_end - f.n0 + 3) / 4 : 0;
     const int P = nrows * f.nseg;
     BfBuf<CPL1> ba, bb;
     prime_passes(f, P, ba, bb);
+    f.tag = st.tag;
     stage_x(p, st, L, xs, false, g0, nr);
     drive_passes(f, P, ba, bb);
   }
 }
 
-// Routed FC1 + SwiGLU of row group g (16 rows of I) of active expert a, for
-// all of the expert's rows (RG at a time).
-template <int RG, bool FULL>
-__device__ __forceinline__ void routed_fc1_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g) {
-  // batch 1: active expert a has exactly one row, its slot (no LDS row list, no barrier)
-  const int slot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[a]]);
+// The next unit of the queue, which thread 0 claimed at the top of the
+// current one, posted for the waves to read in the middle of the unit
+// (unext relative to n_static, as claimed): the
+// word carries the unit-loop iteration it belongs to, and a wave polls LDS
+// until it shows the current one.  One word serves every iteration: all of
+// iteration i's reads come before the barrier that ends i, and iteration
+// i + 1's write after it.
+__device__ __forceinline__ void post_next(const LayerParams& p, Lds& L, int it, unsigned unext) {
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&L.pre, ((uint64_t)(uint32_t)(it + 1) << 32) | (uint32_t)(p.n_static + (int)unext),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ int read_next(Lds& L, int it) {
+  uint64_t v;
+  while (((v = __hip_atomic_load(&L.pre, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >> 32) !=
+         (uint64_t)(uint32_t)(it + 1))
+    __builtin_amdgcn_s_sleep(1);
+  return __builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+
+// Passes of wave w in a batch-1 routed FC1 unit: wave w takes segments w,
+// w + 4, w + 8, ... (Fc1Tile::seg); at H 7168 (14 segments) 4, 4, 3 and 3.
+__device__ __forceinline__ int fc1_passes(int S1, int w) { return w < S1 ? (S1 - w + 3) / 4 : 0; }
+
+// One routed FC1 + SwiGLU unit at batch 1 (row group g of active expert a).
+// `held`: the unit before already issued this unit's first two passes into
+// the tile buffers.  The wave's refills run two passes ahead; when its pass
+// count P is even (>= 2) the last two refills of the unit take the first two
+// passes of the next unit of the queue instead, if that is a routed FC1 unit
+// too (`nfc1`, resolved from the posted next index just before the first of
+// them; pass 0 then lands in buffer a, pass 1 in b).  So the stream of the
+// waves that set the unit's length (4 passes at H 7168) goes on across the
+// unit boundary instead of draining, and the next unit starts with their
+// data already in flight.  Waves with an odd count (3 passes, one pass of
+// slack) load their first passes at the unit's start: handing those on too,
+// or re-dealing the segments 4, 4, 4, 2 so that every wave hands on, measured
+// no better, as did claiming the queue in pairs.
+//
+// Thread 0 posts the next unit index (`unext`, claimed at the top of the
+// unit) for the other waves at wave 0's pass 1 (pass 0 if P < 3): reading
+// the claim's result waits for every load issued before it, and by then the
+// wave needs the first two passes' data anyway.  Wave 0 always has a pass,
+// posts before it resolves, and waits for no other wave between the unit's
+// start and the post, so every wave's poll ends.
+template <bool FULL>
+__device__ __forceinline__ void fc1_unit_b1(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g, int it,
+                                            unsigned unext, bool held, TileBuf1& ba, TileBuf1& bb, bool& nfc1) {
+  const int slot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[a]]);  // batch 1: one row per expert
   const uint8_t* blob = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[a]) * p.blob_bytes;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // w: wave-uniform (scalar)
   const int C1 = p.H / 32, S1 = (C1 + 15) / 16;
-  const int P = w < S1 ? (S1 - w + 3) / 4 : 0;
-  {
-    Fc1Tile<RG, FULL> f;
-    f.blob = blob;
-    f.C1 = C1;
-    f.g = g;
-    f.w = w;
-    f.xs = xs;
-    f.xstride = p.xstride;
-    f.ag = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    f.au = f.ag;
-    TileBuf1 ba, bb;
-    prime_passes(f, P, ba, bb);
-    stage_x(p, st, L, xs, true, 0, 1);
-    drive_rolling(f, P, ba, bb);
-    if ((lane & 15) == 0) {  // column 0: lane 16 q holds rows 4 q .. 4 q + 3
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        L.red[w][0][4 * (lane >> 4) + i][0] = f.ag[i];
-        L.red[w][0][4 * (lane >> 4) + i][1] = f.au[i];
+  const int P = fc1_passes(S1, w);
+  const int base = p.n_rt + p.n_ro + p.n_sch + p.n_s1, n1 = st.U * p.T1;
+  Fc1Tile<1, FULL> f;
+  f.blob = blob;
+  f.C1 = C1;
+  f.g = g;
+  f.w = w;
+  f.xs = xs;
+  f.xstride = p.xstride;
+  f.ag = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  f.au = f.ag;
+  if (!held) prime_passes(f, P, ba, bb);
+  stage_x(p, st, L, xs, true, 0, 1);
+  const bool hand_on = P >= 2 && (P & 1) == 0;
+  bool resolved = false;
+  const uint8_t* nblob = blob;
+  int ng = 0;
+  nfc1 = false;
+  const int post_pp = P >= 3 ? 1 : 0;
+  // pass pp's refill: this unit's pass pp + 2, or pass pp + 2 - P (0 or 1) of the next
+  auto step = [&](TileBuf1& b, int pp) {
+    const int q = pp + 2;
+    if (pp == post_pp) post_next(p, L, it, unext);
+    if (q >= P && !resolved && hand_on) {
+      resolved = true;
+      const int rn = read_next(L, it) - base;
+      if ((unsigned)rn < (unsigned)n1) {
+        const int an = rn / p.T1;
+        ng = rn - an * p.T1;
+        nblob = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[an]) * p.blob_bytes;
+        nfc1 = true;
       }
     }
+    const bool own = q < P;
+    const int s2 = f.seg(own ? q : q - P);
+    const int SC2 = FULL ? 16 : min(16, C1 - 16 * s2);
+    f.math(b, pp, own || nfc1, (own ? blob : nblob) + 2 * tile_off(own ? g : ng, s2, C1), SC2);
+  };
+  for (int pp = 0; pp < P; pp += 2) {
+    step(ba, pp);
+    if (pp + 1 < P) step(bb, pp + 1);
+  }
+  if ((lane & 15) == 0) {  // column 0: lane 16 q holds rows 4 q .. 4 q + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      L.red[w][0][4 * (lane >> 4) + i][0] = f.ag[i];
+      L.red[w][0][4 * (lane >> 4) + i][1] = f.au[i];
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < 16) {
+    const int row = threadIdx.x;
+    float vg = 0.0f, vu = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      vg += L.red[ww][0][row][0];
+      vu += L.red[ww][0][row][1];
+    }
+    st_pair_f32(p.hr_p + (size_t)slot * p.I + 16 * g + row, silu_f(vg) * vu, st.tag);
+  }
+  // L.red is next written by a later unit, after the unit loop's barrier
+}
+
+// Routed FC1 + SwiGLU at batch 1 over a run of consecutive units of the
+// queue that are all routed FC1 units, unit u first (its successor already
+// claimed into thread 0's `nxt`).  Each unit hands its two tile buffers on to
+// the next (fc1_unit_b1), so they stay live only inside this loop.  The
+// unit-loop protocol is kept unit by unit: at the end publish the claimed
+// next index, take the barrier, advance `it`, claim the one after.  Returns
+// the first unit index that is not a routed FC1 unit, claimed but not
+// started (its successor not yet claimed).
+template <bool FULL>
+__device__ __forceinline__ int routed_fc1_run(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int u, int& it,
+                                              unsigned& nxt) {
+  const int base = p.n_rt + p.n_ro + p.n_sch + p.n_s1, n1 = st.U * p.T1;
+  TileBuf1 b0, b1;
+  bool held = false;
+  for (;;) {
+    const int rel = u - base, a = rel / p.T1, g = rel - a * p.T1;
+    bool next_held;
+    fc1_unit_b1<FULL>(p, st, L, xs, a, g, it, nxt, held, b0, b1, next_held);
+    held = next_held;
+    if (threadIdx.x == 0) L.nxt[it & 1] = p.n_static + (int)nxt;
     __syncthreads();
-    if ((int)threadIdx.x < 16) {
-      const int r = 0, row = threadIdx.x;
-      float vg = 0.0f, vu = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        vg += L.red[ww][r][row][0];
-        vu += L.red[ww][r][row][1];
-      }
-      st_pair_f32(p.hr_p + (size_t)slot * p.I + 16 * g + row, silu_f(vg) * vu, st.tag);
-    }
-    // L.red is next written by a later unit, after the unit loop's barrier
+    u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);
+    ++it;
+    if ((unsigned)(u - base) >= (unsigned)n1) return u;
+    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1202,13 +1298,13 @@ __device__ __forceinline__ void shared_fc2_unit(const LayerParams& p, WgState& s
     f.nr = nr;
     for (int r = 0; r < RG; ++r) f.acc[r] = 0.0f;
     f.out = p.os_p;
-    f.tag = st.tag;
     f.out_ld = p.H;
     f.row = L.slot + g0;
     const int groups = (m_end - m_begin + 31) / 32;  // 32 rows per block pass (4 waves x 8)
     const int P = m_begin < m_end ? groups * f.nseg : 0;
     BfBuf<CPL2> ba, bb;
     prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
+    f.tag = st.tag;
     stage_h(p, st, hs, p.hs_p, L, g0, nr, p.Is);
     drive_passes(f, P, ba, bb);
   }
@@ -2234,9 +2330,9 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   char* mfb = reinterpret_cast<char*>(lds_raw);  // MFMA staging (aliases the x region: one unit at a time)
   int* sched_lds = reinterpret_cast<int*>(reinterpret_cast<char*>(lds_raw) + p.lds_sched_off);
   __shared__ Lds L;
-  // Every thread loads the call epoch itself: the value is only needed by the
-  // first hand-over, so the load overlaps the first unit's weight loads
-  // instead of costing a round trip (and a barrier) before any of them.
+  // Every thread loads the call epoch itself (no barrier before the first
+  // unit).  A tag computed lazily at its first use, after the first unit's
+  // loads, measured no faster: the wait it saves hides in the set-up code.
   const uint32_t epoch = ld_coh(p.ctrl + CTRL_EPOCH);
   const uint32_t tag = (epoch == 0xFFFFFFFFu) ? 1u : epoch + 1u;  // never 0: a cleared workspace holds no valid pair
   WgState st{false, false, 0, tag, nullptr, nullptr, nullptr, nullptr};
@@ -2251,6 +2347,15 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   }
   int it = 0;
   for (;;) {
+    // Batch > 1 (and partial tiles): the shape is taken through an empty asm
+    // at every unit, so the compiler computes what each unit derives from it
+    // inside that unit instead of hoisting all of it, for every unit type, to
+    // the kernel's start (where it held every workgroup ~2 us at launch and
+    // spilled registers): no vector registers spill then, and batch 8 / 64
+    // run ~1% faster.  The batch-1 kernel at full tiles keeps the hoisting:
+    // there recomputing per unit costs more than the set-up saves (78.5
+    // against 75 us a layer).
+    if constexpr (MF || !FULL) asm volatile("" : "+s"(p.H), "+s"(p.I), "+s"(p.E), "+s"(p.k), "+s"(p.Is), "+s"(p.B));
     // the next unit is claimed now; its index is only needed after this one
     if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int rel = u;
@@ -2296,7 +2401,10 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
         }
       } else {
         if (rel < U * p.T1) {
-          routed_fc1_unit<RG, FULL>(p, st, L, xs, rel / p.T1, rel % p.T1);
+          // a run of routed FC1 units, ending with the loop's protocol done
+          // for each; u is then the next unit, claimed but not started
+          u = routed_fc1_run<FULL>(p, st, L, xs, u, it, nxt);
+          continue;
         } else if ((rel -= U * p.T1) < p.n_s2) {
           shared_fc2_unit<RG, FULL>(p, st, L, hs, rel);
         } else if ((rel -= p.n_s2) < U * p.n_r2) {
@@ -2324,7 +2432,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     if (old == gridDim.x - 1) {
       st_coh(p.ctrl + CTRL_HEAD, 0u);
       st_coh(p.ctrl + CTRL_EXIT, 0u);
-      st_coh(p.ctrl + CTRL_EPOCH, st.tag);  // the next call's tag is L.tag + 1
+      st_coh(p.ctrl + CTRL_EPOCH, st.tag);  // the next call's tag is this one's + 1
     }
   }
 }

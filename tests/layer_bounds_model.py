@@ -49,6 +49,16 @@ def tile_off(g, s, C):
     return g * 16 * C * 17 + s * 16 * 272
 
 
+def fc1_passes(S1, w):
+    """layer.hip fc1_passes: batch-1 routed FC1 passes of wave w."""
+    return (S1 - w + 3) // 4 if w < S1 else 0
+
+
+def fc1_seg(w, p):
+    """layer.hip Fc1Tile::seg: segment of wave w's pass p."""
+    return w + 4 * p
+
+
 def h_lo_offset(K):
     return ((K // 8 + 7) // 8) * 8
 
@@ -498,11 +508,14 @@ def _routed_fc1_b1(chk, p: Params, sched: Schedule, a: int, g: int, nb: int, xs:
     for c in range(H // 8):
         chk("lds", xs + 16 * swz(c), 16)
         chk("x", 16 * c, 16)
+    # Passes 0 and 1 of a wave with an even pass count may be issued by the
+    # unit before (the hand-on of fc1_unit_b1) when that was a routed FC1 unit
+    # too: the same addresses, computed from the same schedule entry.
     for t, w, lane in _lanes():
-        P = (S1 - w + 3) // 4 if w < S1 else 0
+        P = fc1_passes(S1, w)
         q = lane >> 4
         for pp in range(P):
-            s = w + 4 * pp
+            s = fc1_seg(w, pp)
             SC = min(16, C1 - 16 * s)
             gt = blob + 2 * tile_off(g, s, C1)
             _load_tile(chk, "experts", gt, SC, lane)

@@ -189,6 +189,32 @@ def test_k3_deterministic(k3_layer):
         assert np.array_equal(out.view(np.uint32), first.view(np.uint32))
 
 
+def test_k3_deterministic_batch1_back_to_back(k3_layer):
+    """100 batch-1 calls enqueued back to back on one workspace, alternating
+    two inputs (the routed FC1 units hand their tile buffers on to the next
+    unit of the queue): every call bit-identical to a lone synchronised call
+    on the same input, and no wait gave up."""
+    import torch
+    cfg = CONFIGS["k3_b1"]
+    print("[case] layer K3 B1 determinism x100 back to back", flush=True)
+    xs = [_dev(x_host(cfg, 0, variant=v)) for v in (5, 6)]
+    res0 = [_dev(residual_from_x(x_host(cfg, 0, variant=v))) for v in (5, 6)]
+    ws = moe.alloc_workspace(k3_layer, 1)
+    ref = []
+    for v in range(2):
+        r = res0[v].clone()
+        moe.moe_decode_layer(k3_layer, xs[v], r, ws=ws)
+        torch.cuda.synchronize()
+        ref.append(r.view(torch.int32).clone())
+    outs = [res0[i % 2].clone() for i in range(100)]
+    for i in range(100):
+        moe.moe_decode_layer(k3_layer, xs[i % 2], outs[i], ws=ws)
+    torch.cuda.synchronize()
+    for i in range(100):
+        assert torch.equal(outs[i].view(torch.int32), ref[i % 2]), i
+    assert moe.workspace_status(ws) == 0
+
+
 def test_k3_deterministic_batch64_zipf(k3_layer):
     """50 calls of the batch-64 Zipf layer on one workspace (the hottest
     expert's rows spread over four column groups, ~240 active experts): every

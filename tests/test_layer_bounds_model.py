@@ -8,6 +8,7 @@ groups of one expert."""
 import numpy as np
 import pytest
 
+import layer_bounds_model as M
 from layer_bounds_model import OutOfBounds, Shape, build_schedule, check_call, launch_shape
 
 
@@ -71,3 +72,15 @@ def test_lds_layout_matches_the_kernel_constants():
     assert ls["full"] and ls["rg"] == 1
     ls64 = launch_shape(Shape(H=7168, I=1536, E=896, k=16, Is=1536, B=64))
     assert ls64["full"] and ls64["rg"] == 4 and ls64["lds_h_off"] >= 33280
+
+
+def test_batch1_fc1_segments_cover_each_segment_once():
+    """The batch-1 routed FC1 segment map gives every segment of a row group to
+    exactly one (wave, pass); at H 7168 (14 segments) the waves take 4, 4, 3
+    and 3 passes, and the two with an even count hand their buffers on."""
+    for S1 in range(1, 80):
+        seen = []
+        for w in range(4):
+            seen += [M.fc1_seg(w, p) for p in range(M.fc1_passes(S1, w))]
+        assert sorted(seen) == list(range(S1))
+    assert [M.fc1_passes(14, w) for w in range(4)] == [4, 4, 3, 3]
