@@ -801,7 +801,15 @@ __device__ __forceinline__ void stage_h_split(const LayerParams& p, const WgStat
 template <bool OPQ>
 __device__ __forceinline__ void build_schedule(const LayerParams& p, const WgState& st, int* cnt, int* wtot /* LDS [12] */) {
   const int TID_ = OPQ ? tidx() : (int)threadIdx.x;
-  int* start = cnt + p.E;
+  // Per expert, the set of batch rows that picked it (bit r: row r; a row
+  // picks an expert at most once): its size is the expert's row count, and a
+  // slot's place in the expert's row list is the number of lower rows in the
+  // set, so every call lists an expert's rows in row order whatever order the
+  // threads run in.  Which rows share a column group is then the same on
+  // every call, and so are the results (the narrow and wide FC2 paths sum in
+  // different orders).
+  uint64_t* rowset = reinterpret_cast<uint64_t*>(cnt);  // [E], 8-byte aligned (the LDS region's start)
+  int* start = cnt + 2 * p.E;
   int* ids = start + p.E;
   const int t = TID_, nslots = p.B * p.k;
   bool ok = true;
@@ -814,18 +822,19 @@ __device__ __forceinline__ void build_schedule(const LayerParams& p, const WgSta
       if (base + 256 * i < nslots) ids[base + 256 * i] = (int)min((uint32_t)v[i], (uint32_t)p.E - 1u);
   }
   if (!ok) set_error(p);
-  for (int e = t; e < p.E; e += 256) cnt[e] = 0;
+  for (int e = t; e < p.E; e += 256) rowset[e] = 0ull;
   __syncthreads();
-  for (int s = t; s < nslots; s += 256) atomicAdd(&cnt[ids[s]], 1);
+  for (int s = t; s < nslots; s += 256) atomicOr(reinterpret_cast<unsigned long long*>(&rowset[ids[s]]), 1ull << (s / p.k));
   __syncthreads();
   const int per = (p.E + 255) / 256, e0 = t * per;
   int run_rows = 0, run_act = 0, run_cg = 0;  // rows, active experts, column groups
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e < p.E) {
-      run_rows += cnt[e];
-      run_act += cnt[e] > 0;
-      run_cg += (cnt[e] + 15) >> 4;
+      const int ce = __popcll(rowset[e]);
+      run_rows += ce;
+      run_act += ce > 0;
+      run_cg += (ce + 15) >> 4;
     }
   }
   const int lane = t & 63, w = t >> 6;
@@ -855,15 +864,16 @@ __device__ __forceinline__ void build_schedule(const LayerParams& p, const WgSta
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e < p.E) {
+      const int ce = __popcll(rowset[e]);
       start[e] = pr;
-      if (cnt[e] > 0) {
+      if (ce > 0) {
         st_coh(p.active + pa, e);
         st_coh(p.row_off + pa, pr);
         st_coh(p.cg_off + pa, pc);
         ++pa;
       }
-      pr += cnt[e];
-      pc += (cnt[e] + 15) >> 4;
+      pr += ce;
+      pc += (ce + 15) >> 4;
     }
   }
   if (t == 255) {
@@ -872,8 +882,8 @@ __device__ __forceinline__ void build_schedule(const LayerParams& p, const WgSta
   }
   __syncthreads();
   for (int s = t; s < nslots; s += 256) {
-    const int pos = atomicAdd(&start[ids[s]], 1);
-    st_coh(p.rows + pos, s);
+    const int e = ids[s], r = s / p.k;
+    st_coh(p.rows + start[e] + __popcll(rowset[e] & ((1ull << r) - 1ull)), s);
   }
   // publish: every thread's schedule stores complete, then the ready word
   __builtin_amdgcn_s_waitcnt(0);
@@ -1739,8 +1749,12 @@ __device__ __forceinline__ void mf2_load(const LayerParams& p, const uint8_t* do
 
 // hb / lob: this lane's column of the staged h hi / lo halves (column stride
 // applied); hoff: byte offset of segment s inside the column; live: the
-// column exists (else the B fragments are zero).
-template <bool FP4, bool FULL>
+// column exists (else the B fragments are zero).  PK (at most 8 columns):
+// the B operand carries the hi half of column c in column c and the lo half
+// in column c + 8 -- hb is then the lane's own half, lob unused -- so one
+// MFMA a step does what the hi + lo pair does, and column c's result is
+// column c plus column c + 8 of the product (added at the end of the unit).
+template <bool FP4, bool FULL, bool PK = false>
 __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBuf& b, const char* hb, const char* lob,
                                          int hoff, bool live, f32x4 (&acc)[2]) {
   const int lane = tidx() & 63, q = lane >> 4;
@@ -1755,7 +1769,7 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
       const bool bv = live && (FULL || c < SC);
       const int off = after(hoff + (bv ? (128 * kb + 32 * q + 8 * d) * 2 : 0), acc[0][0] + acc[1][0]);
       rh[i] = *reinterpret_cast<const u32x4*>(hb + off);
-      rl[i] = *reinterpret_cast<const u32x4*>(lob + off);
+      if (!PK) rl[i] = *reinterpret_cast<const u32x4*>(lob + off);
     };
 #pragma unroll
     for (int i = 0; i < MF_LA; ++i) rd(i);
@@ -1772,12 +1786,11 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
         if (i + MF_LA < 16) rd(i + MF_LA);
         const bool bv = live && (FULL || c < SC);
         const bf16x8 hi = __builtin_bit_cast(bf16x8, bv ? rh[i] : z);
-        const bf16x8 lo = __builtin_bit_cast(bf16x8, bv ? rl[i] : z);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const bf16x8 wv = fp4x8_bf16(b.q[t][kb][d] & msk, sc[t]);
           acc[t] = mfma_bf16(wv, hi, acc[t]);
-          acc[t] = mfma_bf16(wv, lo, acc[t]);
+          if (!PK) acc[t] = mfma_bf16(wv, __builtin_bit_cast(bf16x8, bv ? rl[i] : z), acc[t]);
         }
       }
     }
@@ -1787,14 +1800,15 @@ __device__ __forceinline__ void mf2_math(const LayerParams& p, int s, const MfBu
       const bool ok = s * 128 + 32 * j + 8 * q < p.Is;
       const int off = hoff + (ok ? (32 * j + 8 * q) * 2 : 0);
       const u32x4 rh = *reinterpret_cast<const u32x4*>(hb + off);
-      const u32x4 rl = *reinterpret_cast<const u32x4*>(lob + off);
       const bf16x8 hi = __builtin_bit_cast(bf16x8, (live && ok) ? rh : z);
-      const bf16x8 lo = __builtin_bit_cast(bf16x8, (live && ok) ? rl : z);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 wv = __builtin_bit_cast(bf16x8, ok ? b.q[t][j] : z);
         acc[t] = mfma_bf16(wv, hi, acc[t]);
-        acc[t] = mfma_bf16(wv, lo, acc[t]);
+        if (!PK) {
+          const u32x4 rl = *reinterpret_cast<const u32x4*>(lob + off);
+          acc[t] = mfma_bf16(wv, __builtin_bit_cast(bf16x8, (live && ok) ? rl : z), acc[t]);
+        }
       }
     }
   }
@@ -1876,7 +1890,10 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
   };
   MfBuf ba, bb;
   const int XF = K * 2 + 16;  // column stride of whole-K staging
-  const bool narrow = 2 * nc * XF <= MF_STAGE_BYTES;
+  // narrow: all of K staged once, at most 8 columns (the packed hi + lo of
+  // mf2_math); 1024 columns never fit (written as a select: the plain
+  // conjunction made the compiler spill 31 VGPRs)
+  const bool narrow = 2 * (nc <= 8 ? nc : 1024) * XF <= MF_STAGE_BYTES;
   {  // the weights do not depend on FC1.  The second pass is tile 1 at
      // segment 0 on the wide FP4 path (chunk order), else tile 0 at segment 1.
     int gt[2];
@@ -1902,15 +1919,16 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
   }
   const float* hsrc = FP4 ? reinterpret_cast<const float*>(p.hr_p) : reinterpret_cast<const float*>(p.hs_p);
   const f32x4 zero4{0.f, 0.f, 0.f, 0.f};
-  if (narrow) {  // all of h staged once; passes tile by tile
+  if (narrow) {  // all of h staged once; passes tile by tile; hi and lo in one MFMA
     constexpr int KS = FP4 ? 512 : 128;
     const int P = MT * S;
-    const bool live = r < nc;
+    const int cc = r & 7;  // lane r < 8: hi half of column r; lane r >= 8: lo half of column r - 8
+    const bool live = cc < nc;
     f32x4 acc[2] = {zero4, zero4};
     __syncthreads();
     mf_stage_h<16>(p, L, hsrc, K, 0, K, nc, nc, mfb, XF, nc * XF);
     __syncthreads();
-    const char* hcol = mfb + (live ? r : 0) * XF;
+    const char* hcol = mfb + (live ? cc : 0) * XF + (r >= 8 ? nc * XF : 0);
     for (int pp = 0; pp < P; pp += 2) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1918,14 +1936,20 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
         if (ps < P) {
           MfBuf& b = h ? bb : ba;
           const int mt = ps / S, sg = ps - mt * S;
-          mf2_math<FP4, FULL>(p, sg, b, hcol, hcol + nc * XF, sg * KS * 2, live, acc);
+          mf2_math<FP4, FULL, true>(p, sg, b, hcol, nullptr, sg * KS * 2, live, acc);
           if (ps + 2 < P) {
             int gt[2];
             groups((ps + 2) / S, gt);
             mf2_load<FP4, FULL>(p, down, gt, (ps + 2) % S, b, acc[0][0] + acc[1][0]);
           }
           if (sg == S - 1) {
-            emit(mt, acc);
+            f32x4 sum[2];  // column c + column c + 8: lanes r and r + 8 of a 16-lane row (rotate by 8)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                sum[tt][i] = acc[tt][i] + __uint_as_float(dpp_u32<0x128>(__float_as_uint(acc[tt][i])));
+            emit(mt, sum);
             acc[0] = zero4;
             acc[1] = zero4;
           }
@@ -2463,8 +2487,8 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B, bool 
   if (!mf && 2 * h_lo_offset(I) > s.hstride) s.hstride = 2 * h_lo_offset(I);  // bf16 hi + lo rows (routed FC2)
   size_t x_bytes = mf ? 0 : (size_t)s.rg * s.xstride * 16;  // matrix-core kernel: no x rows in LDS
   // routing reuses this region: top-k survivors and slots, then the
-  // schedule's counts (2E) and slot ids (B*k)
-  size_t keys_bytes = (size_t)topk_lds_words(E <= 1024 ? 4 : 16) * 4, cnt_bytes = (size_t)(2 * E + B * k) * 4;
+  // schedule's row sets (8 bytes an expert), starts (E) and slot ids (B*k)
+  size_t keys_bytes = (size_t)topk_lds_words(E <= 1024 ? 4 : 16) * 4, cnt_bytes = (size_t)(3 * E + B * k) * 4;
   size_t sched_bytes = keys_bytes > cnt_bytes ? keys_bytes : cnt_bytes;
   size_t xr = x_bytes > sched_bytes ? x_bytes : sched_bytes;
   // batch > 1: the MFMA staging buffers (two 16-column segments) alias this

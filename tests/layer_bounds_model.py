@@ -126,7 +126,7 @@ def launch_shape(sh: Shape):
         hstride = 2 * h_lo_offset(I)
     x_bytes = 0 if B > 1 else rg * xstride * 16
     keys = topk_lds_words(4 if E <= 1024 else 16) * 4
-    cnt = (2 * E + B * k) * 4
+    cnt = (3 * E + B * k) * 4
     xr = max(x_bytes, max(keys, cnt))
     if B > 1:
         xr = max(xr, MF_STAGE_BYTES)
@@ -348,10 +348,10 @@ def check_call(sh: Shape, idx: List[List[int]], bias: bool = False) -> int:
         for s in range(B * k):
             chk("idx_p", 8 * s, 8)
         for e in range(E):
-            chk("lds", xs + 4 * e, 4)
-            chk("lds", xs + 4 * (E + e), 4)
+            chk("lds", xs + 8 * e, 8)  # row set (8 bytes an expert)
+            chk("lds", xs + 4 * (2 * E + e), 4)  # start
         for s in range(B * k):
-            chk("lds", xs + 4 * (2 * E + s), 4)
+            chk("lds", xs + 4 * (3 * E + s), 4)  # slot ids
         chk("ctrl", 4 * 96, 8)
     for u in range(p.n_s1):
         chk.where = f"shared FC1 unit {u}"
@@ -724,7 +724,7 @@ def _mf_fc2(chk, p: Params, sched: Schedule, a: int, cg: int, t: int, nb: int):
     slots = _load_cols(chk, p, sched, a, cg)
     nc = len(slots)
     XF = K * 2 + 16
-    narrow = 2 * nc * XF <= MF_STAGE_BYTES
+    narrow = 2 * (nc if nc <= 8 else 1024) * XF <= MF_STAGE_BYTES
     ntile = (K + MF_NT1 - 1) // MF_NT1 if FP4 else (K + 15) // 16
     for ti in range(ntile):
         _hflag(chk, p, a if FP4 else p.umax, cg, ti)
@@ -791,12 +791,13 @@ def _mf_fc2(chk, p: Params, sched: Schedule, a: int, cg: int, t: int, nb: int):
         stage(0, K, nc, XF, nc * XF)
         for tt, w, lane in _lanes():
             r = lane & 15
-            live = r < nc
-            hcol = (r if live else 0) * XF
+            cc = r & 7  # packed hi + lo: lanes r < 8 read the hi half of column r, r >= 8 the lo half of r - 8
+            live = cc < nc
+            hcol = (cc if live else 0) * XF + (nc * XF if r >= 8 else 0)
             for ps in range(MT * S):
                 mt, sg = ps // S, ps % S
                 load(groups(mt, w), sg, lane)
-                math_reads(sg, hcol, hcol + nc * XF, sg * KS * 2, lane, live)
+                math_reads(sg, hcol, hcol, sg * KS * 2, lane, live)
                 if sg == S - 1:
                     emit(mt, w, lane)
     else:
