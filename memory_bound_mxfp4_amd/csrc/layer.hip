@@ -580,6 +580,30 @@ __device__ __forceinline__ int after_u(int idx, uint32_t dep) {
   return idx;
 }
 
+// Output rows of a matrix-core product, regrouped for wide stores.  After a
+// 16x16 MFMA, lane 16 q + r holds rows 4 q .. 4 q + 3 of column r (v[0..3]).
+// regroup_rows gives lane 16 q + r rows 8 h + 2 q and 8 h + 2 q + 1 of column
+// r (h = 0, 1: two calls), so that one 16-byte store per lane writes rows
+// 8 h .. 8 h + 7 of a column as 64 contiguous bytes across lanes r, 16 + r,
+// 32 + r, 48 + r (4 x 8-byte stores at a 32-byte stride wrote every line of
+// the outputs four times over).  Every lane of the wave must take part.
+__device__ __forceinline__ void regroup_rows(const f32x4& v, int h, float& a, float& b) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
+  const int src = 16 * (2 * h + (q >> 1)) + (lane & 15);
+  const float x0 = __shfl(v[0], src), x1 = __shfl(v[1], src), x2 = __shfl(v[2], src), x3 = __shfl(v[3], src);
+  a = (q & 1) ? x2 : x0;
+  b = (q & 1) ? x3 : x1;
+}
+
+// Two consecutive tagged pairs (p 16-byte aligned) in one 16-byte store with
+// the coherence of st_coh's 8-byte atomic stores (written through to the
+// device-coherent level).  A reader polls each 8-byte pair on its own, so it
+// needs no more than each aligned 8-byte half to be written whole.
+__device__ __forceinline__ void st_pair2_f32(uint64_t* p, float a, float b, uint32_t tag) {
+  const u32x4 v{__float_as_uint(a), tag, __float_as_uint(b), tag};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+
 // Drives P passes of a tile stream whose math refills the buffer it has just
 // consumed with the pass after next, slab by slab (math(buf, p, refill)).
 // Two passes stay in flight all the time, also while a pass's math runs.
@@ -1349,12 +1373,15 @@ __device__ __forceinline__ void routed_fc2_unit(const LayerParams& p, WgState& s
     drive_rolling(f, P, ba, bb);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      f32x4 val;  // column 0 (hi part) plus column 1 (lo part): lanes 16 q and 16 q + 1
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // column 0 (hi part) plus column 1 (lo part): lanes 16 q and 16 q + 1
-        const float val = f.acc[t][i] + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(f.acc[t][i])));
+      for (int i = 0; i < 4; ++i) val[i] = f.acc[t][i] + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(f.acc[t][i])));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float a, b;
+        regroup_rows(val, h, a, b);
         if ((lane & 15) == 0 && t < ng)
-          st_pair_f32(p.or_p + (size_t)slot * p.H + 16 * (g0 + 4 * t) + 4 * (lane >> 4) + i, val, st.tag);
+          st_pair2_f32(p.or_p + (size_t)slot * p.H + 16 * (g0 + 4 * t) + 8 * h + 2 * (lane >> 4), a, b, st.tag);
       }
     }
   }
@@ -1876,15 +1903,14 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
   };
   uint64_t* out = FP4 ? p.or_p : p.os_p;
   auto emit = [&](int mt, const f32x4 (&acc)[2]) {
-    if (r < nc) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int g = 8 * (MT2 * t + mt) + w + 4 * tt;
-        if (g < G) {
+    for (int tt = 0; tt < 2; ++tt) {
+      const int g = 8 * (MT2 * t + mt) + w + 4 * tt;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            st_pair_f32(out + (size_t)L.slot[r] * p.H + 16 * g + 4 * q + i, acc[tt][i], st.tag);
-        }
+      for (int h = 0; h < 2; ++h) {
+        float a, b;
+        regroup_rows(acc[tt], h, a, b);
+        if (r < nc && g < G) st_pair2_f32(out + (size_t)L.slot[r] * p.H + 16 * g + 8 * h + 2 * q, a, b, st.tag);
       }
     }
   };
@@ -2321,15 +2347,15 @@ __device__ __forceinline__ void mx_fc2_unit(const LayerParams& p, WgState& st, L
           mf2_load<true, FULL>(p, down, gt, (ps + 2) % S, b, acc[0][0] + acc[1][0]);
         }
         if (sg == S - 1) {
-          if (r < nc) {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-              const int gg = 8 * (MF_MT2 * t + mt) + w + 4 * tt;
-              if (gg < G) {
+          for (int tt = 0; tt < 2; ++tt) {
+            const int gg = 8 * (MF_MT2 * t + mt) + w + 4 * tt;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  st_pair_f32(p.or_p + (size_t)L.slot[r] * p.H + 16 * gg + 4 * q + i, acc[tt][i], st.tag);
-              }
+            for (int h = 0; h < 2; ++h) {
+              float a, b;
+              regroup_rows(acc[tt], h, a, b);
+              if (r < nc && gg < G)
+                st_pair2_f32(p.or_p + (size_t)L.slot[r] * p.H + 16 * gg + 8 * h + 2 * q, a, b, st.tag);
             }
           }
           acc[0] = zero4;

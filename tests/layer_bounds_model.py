@@ -582,10 +582,10 @@ def _routed_fc2_b1(chk, p: Params, sched: Schedule, a: int, v: int, nb: int, hs:
             for i in range(16):
                 c = 4 * (i >> 2) + q
                 chk("lds", hs + 16 * ((lane & 1) * hlo + swz((16 * s + min(c, SC - 1)) * 4 + (i & 3))), 16)
-        if (lane & 15) == 0:
+        if (lane & 15) == 0:  # regroup_rows + st_pair2_f32: rows 8 h + 2 q, + 1 of the tile
             for tt in range(ng):
-                for i in range(4):
-                    chk("or_p", 8 * (slot * H + 16 * (g0 + 4 * tt) + 4 * (lane >> 4) + i), 8)
+                for h in range(2):
+                    chk("or_p", 8 * (slot * H + 16 * (g0 + 4 * tt) + 8 * h + 2 * (lane >> 4)), 16)
 
 
 def _combine(chk, p: Params, b: int, t: int):
@@ -783,8 +783,8 @@ def _mf_fc2(chk, p: Params, sched: Schedule, a: int, cg: int, t: int, nb: int):
             for tt in range(2):
                 g = 8 * (MT2 * t + mt) + w + 4 * tt
                 if g < G:
-                    for i in range(4):
-                        chk("or_p" if FP4 else "os_p", 8 * (slots[r] * H + 16 * g + 4 * q + i), 8)
+                    for h in range(2):  # regroup_rows + st_pair2_f32
+                        chk("or_p" if FP4 else "os_p", 8 * (slots[r] * H + 16 * g + 8 * h + 2 * q), 16)
 
     if narrow:
         KS = 512 if FP4 else 128
