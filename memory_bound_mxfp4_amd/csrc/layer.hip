@@ -595,13 +595,30 @@ __device__ __forceinline__ void regroup_rows(const f32x4& v, int h, float& a, fl
   b = (q & 1) ? x3 : x1;
 }
 
-// Two consecutive tagged pairs (p 16-byte aligned) in one 16-byte store with
-// the coherence of st_coh's 8-byte atomic stores (written through to the
-// device-coherent level).  A reader polls each 8-byte pair on its own, so it
-// needs no more than each aligned 8-byte half to be written whole.
-__device__ __forceinline__ void st_pair2_f32(uint64_t* p, float a, float b, uint32_t tag) {
-  const u32x4 v{__float_as_uint(a), tag, __float_as_uint(b), tag};
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+// 16-byte stores with the coherence of st_coh's 8-byte atomic stores
+// (written through to the device-coherent level), as buffer stores: `base`
+// is wave-uniform (a workspace region), `off` the lane's byte offset in it
+// (16-byte aligned, below 2 GiB).  A buffer store lets the compiler see the
+// store (and keep its registers until the hardware has read them), which a
+// store written in inline asm would not.
+__device__ __forceinline__ void st16_coh(const void* base, uint32_t off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0x10);  // 0x10: sc1
+}
+
+// Two consecutive tagged pairs, pairs idx and idx + 1 (idx even) of `base`, in
+// one 16-byte store.  A reader polls each 8-byte pair on its own, so it needs
+// no more than each aligned 8-byte half to be written whole.
+__device__ __forceinline__ void st_pair2_f32(const uint64_t* base, size_t idx, float a, float b, uint32_t tag) {
+  st16_coh(base, (uint32_t)(idx * 8), u32x4{__float_as_uint(a), tag, __float_as_uint(b), tag});
+}
+
+// Four fp32 values, elements idx .. idx + 3 (idx a multiple of 4) of `base`, in
+// one 16-byte store; readers take them only after a flag that the writer sets
+// once all its stores have completed.
+__device__ __forceinline__ void st_f32x4_coh(const float* base, size_t idx, const float (&v)[4]) {
+  st16_coh(base, (uint32_t)(idx * 4),
+           u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
 }
 
 // Drives P passes of a tile stream whose math refills the buffer it has just
@@ -1381,7 +1398,7 @@ __device__ __forceinline__ void routed_fc2_unit(const LayerParams& p, WgState& s
         float a, b;
         regroup_rows(val, h, a, b);
         if ((lane & 15) == 0 && t < ng)
-          st_pair2_f32(p.or_p + (size_t)slot * p.H + 16 * (g0 + 4 * t) + 8 * h + 2 * (lane >> 4), a, b, st.tag);
+          st_pair2_f32(p.or_p, (size_t)slot * p.H + 16 * (g0 + 4 * t) + 8 * h + 2 * (lane >> 4), a, b, st.tag);
       }
     }
   }
@@ -1662,16 +1679,14 @@ __device__ __forceinline__ void mf_fc1_unit(const LayerParams& p, WgState& st, L
       }
     }
   }
-  // h = silu(gate) * up: rows 16 g + 4 q + i of column r, as fp32 (two 8-byte coherent stores)
+  // h = silu(gate) * up: rows 16 g + 4 q + i of column r, as fp32 (one 16-byte coherent store)
   float* hout = FP4 ? reinterpret_cast<float*>(p.hr_p) : reinterpret_cast<float*>(p.hs_p);
   const int n0 = 16 * g + 4 * q;
   if (n0 < N && r < nc) {  // N is a multiple of 8: rows n0 .. n0+3 all exist
     float hv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = silu_f(ag[i]) * au[i];
-    uint64_t* dst = reinterpret_cast<uint64_t*>(hout + (size_t)L.slot[r] * N + n0);
-    st_coh(dst, ((uint64_t)__float_as_uint(hv[1]) << 32) | __float_as_uint(hv[0]));
-    st_coh(dst + 1, ((uint64_t)__float_as_uint(hv[3]) << 32) | __float_as_uint(hv[2]));
+    st_f32x4_coh(hout, (size_t)L.slot[r] * N + n0, hv);
   }
   __builtin_amdgcn_s_waitcnt(0);  // every lane's h stores have completed
   __syncthreads();
@@ -1910,7 +1925,7 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
       for (int h = 0; h < 2; ++h) {
         float a, b;
         regroup_rows(acc[tt], h, a, b);
-        if (r < nc && g < G) st_pair2_f32(out + (size_t)L.slot[r] * p.H + 16 * g + 8 * h + 2 * q, a, b, st.tag);
+        if (r < nc && g < G) st_pair2_f32(out, (size_t)L.slot[r] * p.H + 16 * g + 8 * h + 2 * q, a, b, st.tag);
       }
     }
   };
@@ -2233,16 +2248,14 @@ __device__ __forceinline__ void mx_fc1_unit(const LayerParams& p, WgState& st, L
       }
     }
   }
-  // h = silu(gate) * up: rows 16 g + 4 q + i of column r, as fp32 (two 8-byte coherent stores)
+  // h = silu(gate) * up: rows 16 g + 4 q + i of column r, as fp32 (one 16-byte coherent store)
   float* hout = reinterpret_cast<float*>(p.hr_p);
   const int n0 = 16 * g + 4 * q;
   if (n0 < N && r < nc) {
     float hv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = silu_f(ag[i]) * au[i];
-    uint64_t* dst = reinterpret_cast<uint64_t*>(hout + (size_t)L.slot[r] * N + n0);
-    st_coh(dst, ((uint64_t)__float_as_uint(hv[1]) << 32) | __float_as_uint(hv[0]));
-    st_coh(dst + 1, ((uint64_t)__float_as_uint(hv[3]) << 32) | __float_as_uint(hv[2]));
+    st_f32x4_coh(hout, (size_t)L.slot[r] * N + n0, hv);
   }
   __builtin_amdgcn_s_waitcnt(0);  // every lane's h stores have completed
   __syncthreads();
@@ -2355,7 +2368,7 @@ __device__ __forceinline__ void mx_fc2_unit(const LayerParams& p, WgState& st, L
               float a, b;
               regroup_rows(acc[tt], h, a, b);
               if (r < nc && gg < G)
-                st_pair2_f32(p.or_p + (size_t)L.slot[r] * p.H + 16 * gg + 8 * h + 2 * q, a, b, st.tag);
+                st_pair2_f32(p.or_p, (size_t)L.slot[r] * p.H + 16 * gg + 8 * h + 2 * q, a, b, st.tag);
             }
           }
           acc[0] = zero4;
