@@ -2006,6 +2006,7 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
     // alternating.
     constexpr int XS = 512 * 2 + 16;
     const int NCH = (K + 511) / 512;
+    const bool pk = nc <= 8;
     f32x4 accs[MT2][2];
 #pragma unroll
     for (int i = 0; i < MT2; ++i) accs[i][0] = accs[i][1] = zero4;
@@ -2019,9 +2020,14 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
       for (int j = 0; j < 4; ++j) {
         MfBuf& b = (j & 1) ? bb : ba;
         f32x4 (&acc_j)[2] = accs[FP4 ? j % MT2 : 0];
-        if (pass_ok(c, j))
-          mf2_math<FP4, FULL>(p, seg_of(c, j), b, mfb + r * XS, mfb + MF_COLS * XS + r * XS, FP4 ? 0 : j * 256, true,
-                              acc_j);
+        if (pass_ok(c, j)) {
+          if (pk)  // at most 8 columns: hi and lo in one MFMA (see mf2_math)
+            mf2_math<FP4, FULL, true>(p, seg_of(c, j), b, mfb + (r & 7) * XS + (r >= 8 ? MF_COLS * XS : 0), nullptr,
+                                      FP4 ? 0 : j * 256, true, acc_j);
+          else
+            mf2_math<FP4, FULL>(p, seg_of(c, j), b, mfb + r * XS, mfb + MF_COLS * XS + r * XS, FP4 ? 0 : j * 256, true,
+                                acc_j);
+        }
         const int c2 = j + 2 < 4 ? c : c + 1, j2 = j + 2 < 4 ? j + 2 : j - 2;
         if (pass_ok(c2, j2)) {
           int gt[2];
@@ -2031,8 +2037,18 @@ __device__ __forceinline__ void mf_fc2_unit(const LayerParams& p, WgState& st, L
       }
     }
 #pragma unroll
-    for (int i = 0; i < MT2; ++i)
-      if (i < MT) emit(i, accs[i]);
+    for (int i = 0; i < MT2; ++i) {
+      if (i < MT) {
+        if (pk) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              accs[i][tt][e] += __uint_as_float(dpp_u32<0x128>(__float_as_uint(accs[i][tt][e])));
+        }
+        emit(i, accs[i]);
+      }
+    }
   }
 }
 
