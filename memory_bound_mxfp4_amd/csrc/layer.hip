@@ -621,17 +621,6 @@ __device__ __forceinline__ void st_f32x4_coh(const float* base, size_t idx, cons
            u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
 }
 
-// Drives P passes of a tile stream whose math refills the buffer it has just
-// consumed with the pass after next, slab by slab (math(buf, p, refill)).
-// Two passes stay in flight all the time, also while a pass's math runs.
-template <class Buf, class Traits>
-__device__ __forceinline__ void drive_rolling(Traits& t, int P, Buf& a, Buf& b) {
-  for (int p = 0; p < P; p += 2) {
-    t.math(a, p, p + 2 < P);
-    if (p + 1 < P) t.math(b, p + 1, p + 3 < P);
-  }
-}
-
 // The LDS reads of a pass's activations are software-pipelined one step
 // ahead of the math, and each read's address is tied (through an empty asm)
 // to the accumulator of the step before, so the compiler cannot hoist every
@@ -749,10 +738,12 @@ struct Fc2Tile {
     const int l = threadIdx.x & 63, q = l >> 4, c = 4 * (i >> 2) + q;
     return (l & 1) * hlo + swz((16 * s + (FULL ? c : min(c, SC - 1))) * 4 + (i & 3));
   }
-  __device__ void math(TileBuf2& b, int s, bool refill) {
+  // With `refill`, slab kb of both tiles is refilled as soon as its last
+  // dword is decoded from the tile pair rt0, rt1 (SC2 blocks: a pass two
+  // ahead, of this unit or of the next), the scale vectors after the last slab.
+  __device__ void math(TileBuf2& b, int s, bool refill, const uint8_t* rt0, const uint8_t* rt1, int SC2) {
     const int q = (threadIdx.x & 63) >> 4;
     const int SC = FULL ? 16 : min(16, C2 - 16 * s);
-    const int SC2 = FULL ? 16 : min(16, C2 - 16 * (s + 2));
     u32x4 hv[4], hn[4];  // h granules of this slab and of the next (read one slab ahead)
 #pragma unroll
     for (int d = 0; d < 4; ++d) hv[d] = hs[hg(s, SC, d)];
@@ -779,7 +770,7 @@ struct Fc2Tile {
       if (refill) {
         o = after_u(after_u(o, __builtin_bit_cast(u32x4, wv[0])[3]), __builtin_bit_cast(u32x4, wv[1])[3]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) b.q[t][kb] = load_slab<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s + 2, C2) + o, SC2, kb);
+        for (int t = 0; t < 2; ++t) b.q[t][kb] = load_slab<FULL>((t == 0 ? rt0 : rt1) + o, SC2, kb);
       }
       if (kb < 3) {
 #pragma unroll
@@ -788,7 +779,7 @@ struct Fc2Tile {
     }
     if (refill) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) b.s[t] = load_scales16<FULL>(down + tile_off(g0 + 4 * (t < ng ? t : 0), s + 2, C2) + o, SC2);
+      for (int t = 0; t < 2; ++t) b.s[t] = load_scales16<FULL>((t == 0 ? rt0 : rt1) + o, SC2);
     }
   }
 };
@@ -1361,46 +1352,124 @@ __device__ __forceinline__ void shared_fc2_unit(const LayerParams& p, WgState& s
   }
 }
 
-// Routed FC2 of 8 row groups (128 rows of H) of active expert a: wave w
-// takes groups 8v + w and 8v + w + 4 and runs one pass per segment along I.
-template <int RG, bool FULL>
-__device__ __forceinline__ void routed_fc2_unit(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v) {
+// Routed FC2 at batch 1, unit v of active expert a: 8 row groups (128 rows
+// of H); wave w takes groups 8v + w and 8v + w + 4 and runs one pass per
+// 16-block segment along I (P = 3 at I 1536), two passes in flight.  The h
+// rows alternate between two LDS buffers by unit-loop iteration.
+// `held`: the unit before already issued this unit's passes 0 and 1 (per
+// wave), and `hheld`, staged its h row (all waves).  Handing on: the refills
+// that would run past the unit's last pass take the next queue unit's first
+// two passes instead when that is a routed FC2 unit too -- pass 1 first
+// (into buffer b) when P is odd, so that pass 0 still lands in buffer a --
+// and once the unit's outputs are stored the next unit's h row is staged in
+// the other buffer; so the stream goes on across the unit boundary instead
+// of draining to one pass in flight for the unit's last round trip and then
+// to none while the next unit's h row is read.  The next index comes from
+// thread 0's claim at the top of the unit, posted in LDS at wave 0's pass 1
+// (pass 0 if P < 3), as for FC1.
+template <bool FULL>
+__device__ __forceinline__ void fc2_unit_b1(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v, int it,
+                                            unsigned unext, bool& held, bool& hheld, TileBuf2& ba, TileBuf2& bb) {
   const int slot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[a]]);  // batch 1: the active expert's one row
   const int C1 = p.H / 32, C2 = p.I / 32, S2 = (C2 + 15) / 16;
-  const uint8_t* down = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[a]) * p.blob_bytes +
-                        (size_t)2 * p.I * C1 * 17;
+  const size_t down_off = (size_t)2 * p.I * C1 * 17;
+  const uint8_t* down = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[a]) * p.blob_bytes + down_off;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // w: wave-uniform (scalar)
   const int G = p.H / 16, g0 = 8 * v + w;
   const int ng = g0 < G ? (g0 + 4 < G ? 2 : 1) : 0;
   const int P = ng > 0 ? S2 : 0;
   const int hlo = h_lo_offset(p.I);
-  {
-    Fc2Tile<RG, FULL> f;
-    f.down = down;
-    f.C2 = C2;
-    f.g0 = min(g0, G - 1);
-    f.ng = ng;
-    f.hs = hs;
-    f.hlo = hlo;
-    f.acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    f.acc[1] = f.acc[0];
-    TileBuf2 ba, bb;
-    prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
-    stage_h_split(p, st, hs, p.hr_p, slot, p.I, hlo);
-    drive_rolling(f, P, ba, bb);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x4 val;  // column 0 (hi part) plus column 1 (lo part): lanes 16 q and 16 q + 1
-#pragma unroll
-      for (int i = 0; i < 4; ++i) val[i] = f.acc[t][i] + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(f.acc[t][i])));
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float a, b;
-        regroup_rows(val, h, a, b);
-        if ((lane & 15) == 0 && t < ng)
-          st_pair2_f32(p.or_p, (size_t)slot * p.H + 16 * (g0 + 4 * t) + 8 * h + 2 * (lane >> 4), a, b, st.tag);
+  const int base2 = p.n_rt + p.n_ro + p.n_sch + p.n_s1 + st.U * p.T1 + p.n_s2, n2 = st.U * p.n_r2;
+  u32x4* hcur = hs + (it & 1) * p.hstride;
+  Fc2Tile<1, FULL> f;
+  f.down = down;
+  f.C2 = C2;
+  f.g0 = min(g0, G - 1);
+  f.ng = ng;
+  f.hs = hcur;
+  f.hlo = hlo;
+  f.acc[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  f.acc[1] = f.acc[0];
+  if (!held) prime_passes(f, P, ba, bb);  // the weights do not depend on FC1
+  if (!hheld) stage_h_split(p, st, hcur, p.hr_p, slot, p.I, hlo);
+  bool resolved = false, nfc2 = false, nnext = false;
+  const uint8_t* ndown = down;
+  int ng0 = f.g0, nng = ng, nslot = slot;
+  const int post_pp = P >= 3 ? 1 : 0;
+  // the next unit, from the posted index: is it a routed FC2 unit, and does
+  // this wave have rows in it
+  auto resolve = [&]() {
+    resolved = true;
+    const int rn = read_next(L, it) - base2;
+    if ((unsigned)rn < (unsigned)n2) {
+      const int an = rn / p.n_r2, gn = 8 * (rn - an * p.n_r2) + w;
+      nnext = true;
+      nslot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[an]]);
+      if (gn < G && P >= 2) {
+        ng0 = gn;
+        nng = gn + 4 < G ? 2 : 1;
+        ndown = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[an]) * p.blob_bytes + down_off;
+        nfc2 = true;
       }
     }
+  };
+  auto step = [&](TileBuf2& b, int pp) {
+    const int q = pp + 2;
+    if (pp == post_pp) post_next(p, L, it, unext);
+    if (q >= P && !resolved) resolve();
+    const bool own = q < P;
+    const int s2 = own ? q : ((q - P) ^ (P & 1));
+    const uint8_t* d = own ? down : ndown;
+    const int gg = own ? f.g0 : ng0, gk = own ? ng : nng;
+    f.math(b, pp, own || nfc2, d + tile_off(gg, s2, C2), d + tile_off(gg + (gk > 1 ? 4 : 0), s2, C2),
+           FULL ? 16 : min(16, C2 - 16 * s2));
+  };
+  for (int pp = 0; pp < P; pp += 2) {
+    step(ba, pp);
+    if (pp + 1 < P) step(bb, pp + 1);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 val;  // column 0 (hi part) plus column 1 (lo part): lanes 16 q and 16 q + 1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) val[i] = f.acc[t][i] + __uint_as_float(dpp_u32<0xB1>(__float_as_uint(f.acc[t][i])));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float a, b;
+      regroup_rows(val, h, a, b);
+      if ((lane & 15) == 0 && t < ng)
+        st_pair2_f32(p.or_p, (size_t)slot * p.H + 16 * (g0 + 4 * t) + 8 * h + 2 * (lane >> 4), a, b, st.tag);
+    }
+  }
+  if (!resolved) resolve();  // a wave with no pass (partial last unit) learns the next unit here
+  // every wave read the same index, so all of them stage or none does (the
+  // staging ends with a barrier)
+  if (nnext) stage_h_split(p, st, hs + ((it + 1) & 1) * p.hstride, p.hr_p, nslot, p.I, hlo);
+  held = nfc2;
+  hheld = nnext;
+}
+
+// Routed FC2 at batch 1 over a run of consecutive units of the queue that
+// are all routed FC2 units, unit u first (its successor already claimed into
+// thread 0's `nxt`); the tile buffers are handed from unit to unit
+// (fc2_unit_b1) and stay live only inside this loop.  The unit-loop protocol
+// is kept unit by unit, as in routed_fc1_run.  Returns the first unit index
+// that is not a routed FC2 unit, claimed but not started.
+template <bool FULL>
+__device__ __forceinline__ int routed_fc2_run(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int u, int& it,
+                                              unsigned& nxt) {
+  const int base2 = p.n_rt + p.n_ro + p.n_sch + p.n_s1 + st.U * p.T1 + p.n_s2, n2 = st.U * p.n_r2;
+  TileBuf2 b0, b1;
+  bool held = false, hheld = false;
+  for (;;) {
+    const int rel = u - base2, a = rel / p.n_r2, v = rel - a * p.n_r2;
+    fc2_unit_b1<FULL>(p, st, L, hs, a, v, it, nxt, held, hheld, b0, b1);
+    if (threadIdx.x == 0) L.nxt[it & 1] = p.n_static + (int)nxt;
+    __syncthreads();
+    u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);
+    ++it;
+    if ((unsigned)(u - base2) >= (unsigned)n2) return u;
+    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -2505,7 +2574,9 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
         } else if ((rel -= U * p.T1) < p.n_s2) {
           shared_fc2_unit<RG, FULL>(p, st, L, hs, rel);
         } else if ((rel -= p.n_s2) < U * p.n_r2) {
-          routed_fc2_unit<RG, FULL>(p, st, L, hs, rel / p.n_r2, rel % p.n_r2);
+          // a run of routed FC2 units, as for FC1
+          u = routed_fc2_run<FULL>(p, st, L, hs, u, it, nxt);
+          continue;
         } else if ((rel -= U * p.n_r2) < p.B * p.n_tile) {
           combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile);
         } else {
@@ -2570,7 +2641,8 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B, bool 
   if (mf && mf_bytes > xr) xr = mf_bytes;
   xr = align256(xr);
   s.lds_h_off = (int)xr;
-  size_t hr = mf ? 0 : align256((size_t)s.rg * s.hstride * 16);
+  // batch 1: two h rows (routed FC2 units alternate between them)
+  size_t hr = mf ? 0 : align256((size_t)2 * s.hstride * 16);
   s.lds_sched_off = (int)(xr + hr);
   const size_t slots = (size_t)B * k, umax = slots < (size_t)E ? slots : (size_t)E;
   s.lds = xr + hr + align256(4 * (3 * umax + 2 + slots));

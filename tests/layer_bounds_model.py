@@ -131,7 +131,7 @@ def launch_shape(sh: Shape):
     if B > 1:
         xr = max(xr, MF_STAGE_BYTES)
     xr = align256(xr)
-    hr = 0 if B > 1 else align256(rg * hstride * 16)
+    hr = 0 if B > 1 else align256(2 * hstride * 16)  # batch 1: two h rows, alternating by unit
     slots = B * k
     umax = min(slots, E)
     lds = xr + hr + align256(4 * (3 * umax + 2 + slots))
@@ -566,7 +566,20 @@ def _routed_fc2_b1(chk, p: Params, sched: Schedule, a: int, v: int, nb: int, hs:
     down = sched.active[a] * nb + 2 * I * C1 * 17
     G = H // 16
     hlo = h_lo_offset(I)
-    for e in range(I):  # stage_h_split
+    for hb in (hs, hs + 16 * p.ls["hstride"]):  # either of the two h rows (by unit-loop iteration)
+        _routed_fc2_b1_h(chk, p, sched, a, v, nb, hb, slot, down, hlo)
+
+
+def _routed_fc2_b1_h(chk, p: Params, sched: Schedule, a: int, v: int, nb: int, hs: int, slot: int, down: int,
+                     hlo: int):
+    sh = p.sh
+    H, I = sh.H, sh.I
+    C2 = I // 32
+    S2 = (C2 + 15) // 16
+    G = H // 16
+    # the staged row (hi granules, then lo at hlo) stays inside the h region, clear of the schedule
+    assert p.ls["lds_h_off"] <= hs and hs + 16 * 2 * hlo <= p.ls["lds_sched_off"]
+    for e in range(I):  # stage_h_split (at the unit's start, or at the end of the unit before)
         chk("hr_p", 8 * (slot * I + e), 8)
         chk("lds", hs + 2 * (swz(e >> 3) * 8 + (e & 7)), 2)
         chk("lds", hs + 2 * ((hlo + swz(e >> 3)) * 8 + (e & 7)), 2)
