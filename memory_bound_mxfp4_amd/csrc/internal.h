@@ -36,11 +36,12 @@ struct Sched {
 // Control block at the start of the workspace: uint32 words, each counter on
 // a 128-byte line of its own (line i starts at word CTRL_STRIDE * i) so that
 // polls of different counters never share a cache line.
-//   line 0, word 0   work-queue head                (zero between calls)
+//   line 0, word 0   head of work queue 0           (zero between calls)
 //   line 0, word 7   sticky error word (byte offset MOE_WS_STATUS_OFFSET)
 //   line 1           workgroups that have exited    (zero between calls)
 //   line 2           call epoch: bumped by the last workgroup of every call
 //   line 3           schedule-ready word pair (batch > 1): U | tag << 32
+//   line 4           head of work queue 1           (zero between calls)
 // Data handed between workgroups inside a call travels as 8-byte pairs
 // (32-bit value | 32-bit tag << 32), tag = epoch + 1 of the call, written and
 // read with single 8-byte coherent accesses: a consumer polls the data itself
@@ -48,7 +49,7 @@ struct Sched {
 // its stores and bump a counter.
 constexpr int CTRL_STRIDE = 32;
 constexpr int CTRL_HEAD = 0, CTRL_ERR = 7, CTRL_EXIT = 1 * CTRL_STRIDE, CTRL_EPOCH = 2 * CTRL_STRIDE,
-              CTRL_READY = 3 * CTRL_STRIDE, CTRL_WORDS = 4 * CTRL_STRIDE;
+              CTRL_READY = 3 * CTRL_STRIDE, CTRL_HEAD1 = 4 * CTRL_STRIDE, CTRL_WORDS = 5 * CTRL_STRIDE;
 
 // Workspace of moe_decode_layer.
 struct Workspace {

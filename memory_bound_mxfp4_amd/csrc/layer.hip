@@ -119,6 +119,7 @@ struct LayerParams {
   int mf_cgs;    // batch > 1: shared-expert column groups (16 batch rows each)
   int n_front;   // units before the routed ones (router .. shared FC1)
   int n_static;  // units 0 .. n_static-1 go to workgroups 0 .. n_static-1
+  int nq;        // work queues after them: 2 (1 for a one-workgroup grid)
   int xstride;        // LDS x row stride, 16-byte granules (multiple of 8)
   int hstride;        // LDS h row stride, 16-byte granules (multiple of 8)
   int lds_h_off;      // byte offset of the h staging region in dynamic LDS
@@ -1179,16 +1180,40 @@ __device__ __forceinline__ void shared_fc1_unit(const LayerParams& p, WgState& s
   }
 }
 
+// The units after the static ones form two interleaved work queues with a
+// counter each: workgroup w takes units n_static + q + 2 c (q = w mod 2, c =
+// 0, 1, ... from counter q).  One counter for all workgroups serialised the
+// claims of the batch-1 layer (about 3,300 in ~70 us) enough to cost it ~4
+// us; splitting by workgroup parity keeps both queues' mix of workgroups
+// alike, so they advance together (a split by the workgroup's slot on its CU
+// drifted apart and gained nothing; four and eight queues gained less).  A
+// unit waits only on units of lower index, so the lowest unfinished unit is
+// either claimed (its inputs are done, it completes) or unclaimed with every
+// claimed unit of its queue below it and finished, and then that queue's
+// workgroups are free to take it: no deadlock while each queue has a
+// workgroup (a one-workgroup grid runs one queue).
+__device__ __forceinline__ int queue_id(const LayerParams& p) { return p.nq > 1 ? (int)(blockIdx.x & 1u) : 0; }
+
+__device__ __forceinline__ unsigned claim_next(const LayerParams& p) {
+  return __hip_atomic_fetch_add(p.ctrl + (queue_id(p) ? CTRL_HEAD1 : CTRL_HEAD), 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Unit index of this workgroup's claim number c (claim_next's result).
+__device__ __forceinline__ int queue_unit(const LayerParams& p, unsigned c) {
+  return p.n_static + queue_id(p) + p.nq * (int)c;
+}
+
 // The next unit of the queue, which thread 0 claimed at the top of the
 // current one, posted for the waves to read in the middle of the unit
-// (unext relative to n_static, as claimed): the
+// (unext: thread 0's claim number, as claimed): the
 // word carries the unit-loop iteration it belongs to, and a wave polls LDS
 // until it shows the current one.  One word serves every iteration: all of
 // iteration i's reads come before the barrier that ends i, and iteration
 // i + 1's write after it.
 __device__ __forceinline__ void post_next(const LayerParams& p, Lds& L, int it, unsigned unext) {
   if (threadIdx.x == 0)
-    __hip_atomic_store(&L.pre, ((uint64_t)(uint32_t)(it + 1) << 32) | (uint32_t)(p.n_static + (int)unext),
+    __hip_atomic_store(&L.pre, ((uint64_t)(uint32_t)(it + 1) << 32) | (uint32_t)queue_unit(p, unext),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
@@ -1313,12 +1338,12 @@ __device__ __forceinline__ int routed_fc1_run(const LayerParams& p, WgState& st,
     bool next_held;
     fc1_unit_b1<FULL>(p, st, L, xs, a, g, it, nxt, held, b0, b1, next_held);
     held = next_held;
-    if (threadIdx.x == 0) L.nxt[it & 1] = p.n_static + (int)nxt;
+    if (threadIdx.x == 0) L.nxt[it & 1] = queue_unit(p, nxt);
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);
     ++it;
     if ((unsigned)(u - base) >= (unsigned)n1) return u;
-    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) nxt = claim_next(p);
   }
 }
 
@@ -1464,12 +1489,12 @@ __device__ __forceinline__ int routed_fc2_run(const LayerParams& p, WgState& st,
   for (;;) {
     const int rel = u - base2, a = rel / p.n_r2, v = rel - a * p.n_r2;
     fc2_unit_b1<FULL>(p, st, L, hs, a, v, it, nxt, held, hheld, b0, b1);
-    if (threadIdx.x == 0) L.nxt[it & 1] = p.n_static + (int)nxt;
+    if (threadIdx.x == 0) L.nxt[it & 1] = queue_unit(p, nxt);
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);
     ++it;
     if ((unsigned)(u - base2) >= (unsigned)n2) return u;
-    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) nxt = claim_next(p);
   }
 }
 
@@ -2489,7 +2514,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
   int u = (int)blockIdx.x < p.n_static ? (int)blockIdx.x : -1;
   unsigned nxt = 0;
   if (u < 0) {
-    if (threadIdx.x == 0) L.next = p.n_static + (int)__hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) L.next = queue_unit(p, claim_next(p));
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(L.next);
   }
@@ -2504,9 +2529,9 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     // measured slower: their reads then compete with the router's from the
     // first microsecond.
     if (u >= 0 && u < p.n_rt) {
-      if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) nxt = claim_next(p);
       router_unit(p, st, u);
-      if (threadIdx.x == 0) L.nxt[0] = p.n_static + (int)nxt;
+      if (threadIdx.x == 0) L.nxt[0] = queue_unit(p, nxt);
       __syncthreads();
       u = __builtin_amdgcn_readfirstlane(L.nxt[0]);
       it = 1;
@@ -2523,7 +2548,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     // against 75 us a layer).
     if constexpr (MF || !FULL) asm volatile("" : "+s"(p.H), "+s"(p.I), "+s"(p.E), "+s"(p.k), "+s"(p.Is), "+s"(p.B));
     // the next unit is claimed now; its index is only needed after this one
-    if (threadIdx.x == 0) nxt = __hip_atomic_fetch_add(p.ctrl + CTRL_HEAD, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) nxt = claim_next(p);
     int rel = u;
     if (rel < p.n_rt) {
       if constexpr (MF) {
@@ -2587,7 +2612,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     // One barrier per unit: it ends this unit's use of LDS and publishes the
     // next index.  The index word alternates between two slots, so thread 0
     // cannot overwrite one that a slower wave has yet to read.
-    if (threadIdx.x == 0) L.nxt[it & 1] = p.n_static + (int)nxt;
+    if (threadIdx.x == 0) L.nxt[it & 1] = queue_unit(p, nxt);
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);  // uniform: unit arithmetic stays scalar
     ++it;
@@ -2599,6 +2624,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     const unsigned old = __hip_atomic_fetch_add(p.ctrl + CTRL_EXIT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == gridDim.x - 1) {
       st_coh(p.ctrl + CTRL_HEAD, 0u);
+      st_coh(p.ctrl + CTRL_HEAD1, 0u);
       st_coh(p.ctrl + CTRL_EXIT, 0u);
       st_coh(p.ctrl + CTRL_EPOCH, st.tag);  // the next call's tag is this one's + 1
     }
@@ -2663,6 +2689,7 @@ static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
   }
   const int grid = num_cus() * per_cu;
   p.n_static = std::min(grid, p.n_front);
+  p.nq = grid >= 2 ? 2 : 1;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ MF_COLS, MF_NT1, MF_MT2 = 16, 64, 4
 MF_NT2 = 128 * MF_MT2
 MF_XS_FP4 = 512 * 2 + 16
 MF_STAGE_BYTES = 2 * MF_COLS * MF_XS_FP4
-CTRL_WORDS = 4 * 32
+CTRL_WORDS = 5 * 32  # five 128-byte lines: heads of the two work queues at lines 0 and 4
 RT_F64_MIN_BATCH = 16
 
 
@@ -393,6 +393,7 @@ def check_call(sh: Shape, idx: List[List[int]], bias: bool = False) -> int:
     chk("ctrl", 0, 4)
     chk("ctrl", 4 * 32, 4)
     chk("ctrl", 4 * 64, 4)
+    chk("ctrl", 4 * 128, 4)
     return chk.count
 
 
