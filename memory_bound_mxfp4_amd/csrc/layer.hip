@@ -119,7 +119,7 @@ struct LayerParams {
   int mf_cgs;    // batch > 1: shared-expert column groups (16 batch rows each)
   int n_front;   // units before the routed ones (router .. shared FC1)
   int n_static;  // units 0 .. n_static-1 go to workgroups 0 .. n_static-1
-  int nq;        // work queues after them: 2 (1 for a one-workgroup grid)
+  int nq;        // work queues after them: 2 (1 for grids under 16 workgroups)
   int xstride;        // LDS x row stride, 16-byte granules (multiple of 8)
   int hstride;        // LDS h row stride, 16-byte granules (multiple of 8)
   int lds_h_off;      // byte offset of the h staging region in dynamic LDS
@@ -1181,18 +1181,21 @@ __device__ __forceinline__ void shared_fc1_unit(const LayerParams& p, WgState& s
 }
 
 // The units after the static ones form two interleaved work queues with a
-// counter each: workgroup w takes units n_static + q + 2 c (q = w mod 2, c =
-// 0, 1, ... from counter q).  One counter for all workgroups serialised the
-// claims of the batch-1 layer (about 3,300 in ~70 us) enough to cost it ~4
-// us; splitting by workgroup parity keeps both queues' mix of workgroups
-// alike, so they advance together (a split by the workgroup's slot on its CU
-// drifted apart and gained nothing; four and eight queues gained less).  A
-// unit waits only on units of lower index, so the lowest unfinished unit is
-// either claimed (its inputs are done, it completes) or unclaimed with every
-// claimed unit of its queue below it and finished, and then that queue's
-// workgroups are free to take it: no deadlock while each queue has a
-// workgroup (a one-workgroup grid runs one queue).
-__device__ __forceinline__ int queue_id(const LayerParams& p) { return p.nq > 1 ? (int)(blockIdx.x & 1u) : 0; }
+// counter each: workgroup w takes units n_static + q + 2 c (q = bit 3 of w,
+// c = 0, 1, ... from counter q).  One counter for all workgroups serialised
+// the claims of the batch-1 layer (about 3,300 in ~70 us) enough to cost it
+// ~4-5 us.  Workgroups are dealt to the 8 XCDs in turn, so bit 3 puts half of
+// every XCD's workgroups in each queue, and both queues get the same mix of
+// workgroups (first units, XCDs, counter latency) and advance together; a
+// split by workgroup parity (queue = XCD parity) measured ~1 us slower, a
+// split by the workgroup's slot on its CU drifted apart and gained nothing,
+// and four or eight queues gained less.  A unit waits only on units of lower
+// index, so the lowest unfinished unit is either claimed (its inputs are
+// done, it completes) or unclaimed with every claimed unit of its queue below
+// it and finished, and then that queue's workgroups are free to take it: no
+// deadlock while each queue has a workgroup (grids under 16 workgroups run
+// one queue).
+__device__ __forceinline__ int queue_id(const LayerParams& p) { return p.nq > 1 ? (int)((blockIdx.x >> 3) & 1u) : 0; }
 
 __device__ __forceinline__ unsigned claim_next(const LayerParams& p) {
   return __hip_atomic_fetch_add(p.ctrl + (queue_id(p) ? CTRL_HEAD1 : CTRL_HEAD), 1u, __ATOMIC_RELAXED,
@@ -2689,7 +2692,7 @@ static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
   }
   const int grid = num_cus() * per_cu;
   p.n_static = std::min(grid, p.n_front);
-  p.nq = grid >= 2 ? 2 : 1;
+  p.nq = grid >= 16 ? 2 : 1;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
