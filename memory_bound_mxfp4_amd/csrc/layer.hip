@@ -1254,7 +1254,8 @@ __device__ __forceinline__ int fc1_passes(int S1, int w) { return w < S1 ? (S1 -
 // start and the post, so every wave's poll ends.
 template <bool FULL>
 __device__ __forceinline__ void fc1_unit_b1(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int a, int g, int it,
-                                            unsigned unext, bool held, TileBuf1& ba, TileBuf1& bb, bool& nfc1) {
+                                            unsigned unext, bool held, TileBuf1& ba, TileBuf1& bb, bool& nfc1,
+                                            unsigned& unext2) {
   const int slot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[a]]);  // batch 1: one row per expert
   const uint8_t* blob = p.experts + (size_t)__builtin_amdgcn_readfirstlane(st.s_active[a]) * p.blob_bytes;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // w: wave-uniform (scalar)
@@ -1301,6 +1302,10 @@ __device__ __forceinline__ void fc1_unit_b1(const LayerParams& p, WgState& st, L
     step(ba, pp);
     if (pp + 1 < P) step(bb, pp + 1);
   }
+  // when the next unit is a routed FC1 unit too (the run goes on), the claim
+  // of the one after it goes out now, so its result is in when the next unit
+  // posts it
+  if (threadIdx.x == 0 && (unsigned)(queue_unit(p, unext) - base) < (unsigned)n1) unext2 = claim_next(p);
   if ((lane & 15) == 0) {  // column 0: lane 16 q holds rows 4 q .. 4 q + 3
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1327,26 +1332,30 @@ __device__ __forceinline__ void fc1_unit_b1(const LayerParams& p, WgState& st, L
 // claimed into thread 0's `nxt`).  Each unit hands its two tile buffers on to
 // the next (fc1_unit_b1), so they stay live only inside this loop.  The
 // unit-loop protocol is kept unit by unit: at the end publish the claimed
-// next index, take the barrier, advance `it`, claim the one after.  Returns
-// the first unit index that is not a routed FC1 unit, claimed but not
-// started (its successor not yet claimed).
+// next index, take the barrier, advance `it`.  The claim of the one after is
+// issued by the unit before, after its last pass and only when the run goes
+// on: a claim is a memory round trip (~3-5 us under full streaming), and
+// claimed at the next unit's start its result held every wave at the hand-on
+// (~1.5 us a layer).  Returns the first unit index that is not a routed FC1
+// unit, claimed but not started (its successor not yet claimed).
 template <bool FULL>
 __device__ __forceinline__ int routed_fc1_run(const LayerParams& p, WgState& st, Lds& L, u32x4* xs, int u, int& it,
                                               unsigned& nxt) {
   const int base = p.n_rt + p.n_ro + p.n_sch + p.n_s1, n1 = st.U * p.T1;
   TileBuf1 b0, b1;
   bool held = false;
+  unsigned nxt2 = 0;
   for (;;) {
     const int rel = u - base, a = rel / p.T1, g = rel - a * p.T1;
     bool next_held;
-    fc1_unit_b1<FULL>(p, st, L, xs, a, g, it, nxt, held, b0, b1, next_held);
+    fc1_unit_b1<FULL>(p, st, L, xs, a, g, it, nxt, held, b0, b1, next_held, nxt2);
     held = next_held;
     if (threadIdx.x == 0) L.nxt[it & 1] = queue_unit(p, nxt);
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);
     ++it;
     if ((unsigned)(u - base) >= (unsigned)n1) return u;
-    if (threadIdx.x == 0) nxt = claim_next(p);
+    if (threadIdx.x == 0) nxt = nxt2;  // claimed by the unit before (the run goes on)
   }
 }
 
@@ -1397,7 +1406,8 @@ __device__ __forceinline__ void shared_fc2_unit(const LayerParams& p, WgState& s
 // (pass 0 if P < 3), as for FC1.
 template <bool FULL>
 __device__ __forceinline__ void fc2_unit_b1(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int a, int v, int it,
-                                            unsigned unext, bool& held, bool& hheld, TileBuf2& ba, TileBuf2& bb) {
+                                            unsigned unext, bool& held, bool& hheld, TileBuf2& ba, TileBuf2& bb,
+                                            unsigned& unext2) {
   const int slot = __builtin_amdgcn_readfirstlane(st.s_rows[st.s_row_off[a]]);  // batch 1: the active expert's one row
   const int C1 = p.H / 32, C2 = p.I / 32, S2 = (C2 + 15) / 16;
   const size_t down_off = (size_t)2 * p.I * C1 * 17;
@@ -1472,7 +1482,13 @@ __device__ __forceinline__ void fc2_unit_b1(const LayerParams& p, WgState& st, L
   if (!resolved) resolve();  // a wave with no pass (partial last unit) learns the next unit here
   // every wave read the same index, so all of them stage or none does (the
   // staging ends with a barrier)
-  if (nnext) stage_h_split(p, st, hs + ((it + 1) & 1) * p.hstride, p.hr_p, nslot, p.I, hlo);
+  if (nnext) {
+    // the claim of the unit after next goes out now, beside the next h row's
+    // reads, so its result is in when the next unit posts it (claimed at the
+    // next unit's start it held every wave ~one memory round trip at pass 1)
+    if (threadIdx.x == 0) unext2 = claim_next(p);
+    stage_h_split(p, st, hs + ((it + 1) & 1) * p.hstride, p.hr_p, nslot, p.I, hlo);
+  }
   held = nfc2;
   hheld = nnext;
 }
@@ -1481,23 +1497,25 @@ __device__ __forceinline__ void fc2_unit_b1(const LayerParams& p, WgState& st, L
 // are all routed FC2 units, unit u first (its successor already claimed into
 // thread 0's `nxt`); the tile buffers are handed from unit to unit
 // (fc2_unit_b1) and stay live only inside this loop.  The unit-loop protocol
-// is kept unit by unit, as in routed_fc1_run.  Returns the first unit index
-// that is not a routed FC2 unit, claimed but not started.
+// is kept unit by unit, and the unit before claims the one after next, as in
+// routed_fc1_run.  Returns the first unit index that is not a routed FC2
+// unit, claimed but not started.
 template <bool FULL>
 __device__ __forceinline__ int routed_fc2_run(const LayerParams& p, WgState& st, Lds& L, u32x4* hs, int u, int& it,
                                               unsigned& nxt) {
   const int base2 = p.n_rt + p.n_ro + p.n_sch + p.n_s1 + st.U * p.T1 + p.n_s2, n2 = st.U * p.n_r2;
   TileBuf2 b0, b1;
   bool held = false, hheld = false;
+  unsigned nxt2 = 0;
   for (;;) {
     const int rel = u - base2, a = rel / p.n_r2, v = rel - a * p.n_r2;
-    fc2_unit_b1<FULL>(p, st, L, hs, a, v, it, nxt, held, hheld, b0, b1);
+    fc2_unit_b1<FULL>(p, st, L, hs, a, v, it, nxt, held, hheld, b0, b1, nxt2);
     if (threadIdx.x == 0) L.nxt[it & 1] = queue_unit(p, nxt);
     __syncthreads();
     u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);
     ++it;
     if ((unsigned)(u - base2) >= (unsigned)n2) return u;
-    if (threadIdx.x == 0) nxt = claim_next(p);
+    if (threadIdx.x == 0) nxt = nxt2;  // claimed by the unit before (it hands on only to a routed FC2 unit)
   }
 }
 
