@@ -255,7 +255,9 @@ def test_workspace_reuse_and_status(k3_layer):
         idx, gate = moe.moe_decode_layer(k3_layer, _dev(x), r, ws=ws)
         torch.cuda.synchronize()
         assert moe.workspace_status(ws) == 0
-        assert np.all(ws[:64].cpu().numpy() == 0)  # control block cleared again
+        ctrl = ws[:640].cpu().numpy()
+        # control block cleared again: queue 0 head and status word, exit count, queue 1 head
+        assert np.all(ctrl[:64] == 0) and np.all(ctrl[128:132] == 0) and np.all(ctrl[512:516] == 0)
         ref_idx = oracle_layer_idx(cfg, x)
         assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
