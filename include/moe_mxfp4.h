@@ -181,9 +181,9 @@ moe_status expert_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int n,
 /*
  * moe_workspace_init -- clear a workspace before its first use.
  * The first bytes of a layer workspace are a control block that
- * moe_decode_layer's single persistent kernel synchronises through: a
- * work-queue counter (zero between calls) and a call epoch that every call
- * advances.  Data that workgroups of one call hand to each other is tagged
+ * moe_decode_layer's single persistent kernel synchronises through: the
+ * counters of its two work queues (zero between calls) and a call epoch that
+ * every call advances.  Data that workgroups of one call hand to each other is tagged
  * with that call's epoch, so stale data of an earlier call is never taken
  * for the current call's.  A workspace therefore needs this (or any zero
  * fill of the whole buffer) once after allocation, and again after a call
