@@ -292,7 +292,7 @@ __device__ __forceinline__ void stage_h(const LayerParams& p, const WgState& st,
   for (int base = threadIdx.x; base < total; base += 256 * 8) {
     uint64_t v[8];
     const int n = min(8, (total - base + 255) / 256);
-    ok &= poll_pairs<8>(src, n, [&](int t) {
+    ok &= poll_pairs_cached<8>(src, n, [&](int t) {
       const int i = base + 256 * t;
       const int r = i / K, e = i - r * K;
       return (size_t)L.slot[g0 + r] * K + e;
@@ -810,7 +810,8 @@ __device__ __forceinline__ void stage_h_split(const LayerParams& p, const WgStat
   for (int base = threadIdx.x; base < K; base += 256 * 8) {
     uint64_t v[8];
     const int n = min(8, (K - base + 255) / 256);
-    ok &= poll_pairs<8>(src, n, [&](int t) { return row + base + 256 * t; }, st.tag, v, SPIN_LIMIT, p.ctrl + CTRL_ERR);
+    ok &= poll_pairs_cached<8>(src, n, [&](int t) { return row + base + 256 * t; }, st.tag, v, SPIN_LIMIT,
+                               p.ctrl + CTRL_ERR);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int e = base + 256 * t;

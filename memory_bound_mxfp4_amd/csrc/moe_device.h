@@ -125,6 +125,28 @@ __device__ __forceinline__ bool poll_pairs(const uint64_t* p, int n, Idx idx, ui
   }
 }
 
+// poll_pairs for pairs that many workgroups read: one cached read first
+// (workgroup-scope atomic loads, which may hit in this XCD's L2), and the
+// coherent poll only if a pair does not carry `tag` yet.  A cached copy of a
+// pair that carries this call's tag was fetched after the pair was written
+// (value and tag are one 8-byte word, written by one store), so its value is
+// this call's; a stale copy fails the tag test and the pair is read at the
+// device coherence point instead.  A row of h that every FC2 unit of an
+// expert reads is then fetched from memory about once per XCD, not once per
+// unit.
+template <int N, class Idx>
+__device__ __forceinline__ bool poll_pairs_cached(const uint64_t* p, int n, Idx idx, uint32_t tag, uint64_t (&v)[N],
+                                                  unsigned limit, const unsigned* err) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] = __hip_atomic_load(const_cast<uint64_t*>(p + idx(min(i, n - 1))), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < N; ++i) ok &= (i >= n) || pair_has(v[i], tag);
+  return ok || poll_pairs<N>(p, n, idx, tag, v, limit, err);
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup top-k of one row (4 waves), for the fused layer kernel.  Order:
 // (key desc, index asc) on order-preserving integer keys, so ties go to the
