@@ -322,6 +322,19 @@ moe_status residual_add_rmsnorm_bf16(float* h, const uint16_t* t, int batch, int
                                      void* stream);
 
 /*
+ * moe_set_max_workgroups -- test and diagnostic knob, not needed for decoding:
+ * caps the number of workgroups of the layer kernel (every moe_decode_layer*
+ * entry point) launched after it returns, process-wide, at n; n = 0 restores
+ * the default (two workgroups per compute unit).  The layer's work queue is
+ * built to finish on any grid of at least one workgroup (a unit waits only
+ * on units before it in the queue), and its results do not depend on the
+ * grid; a small grid runs it in a different interleaving, which is what
+ * the knob is for.  n < 0: MOE_ERR_INVALID_ARGUMENT.  Not synchronised
+ * with launches in flight on other host threads.
+ */
+moe_status moe_set_max_workgroups(int n);
+
+/*
  * moe_stream_read_probe -- measurement aid, not part of a decode step: one
  * kernel that reads `bytes` of `buf` once with 16-byte non-temporal loads
  * (blocks_per_cu 256-thread workgroups per compute unit, grid-stride), the

@@ -27,7 +27,7 @@ EXPORTS = ("moe_expert_bytes", "moe_workspace_size", "moe_router_workspace_size"
            "moe_decode_layer_kernel_name", "moe_decode_layer_timed", "moe_workspace_init", "moe_pack_experts",
            "moe_unpack_experts", "rmsnorm_bf16", "dense_gemv_bf16", "residual_add_bf16", "residual_add_rmsnorm_bf16",
            "moe_workspace_status", "moe_stream_read_probe", "moe_decode_layer_noalloc", "moe_decode_layer_mxfp8",
-           "moe_prefetch", "moe_status_string")
+           "moe_prefetch", "moe_set_max_workgroups", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +78,7 @@ def load():
         "moe_decode_layer_noalloc": (I, [P, P, P, I, P, P, P, P]),
         "moe_decode_layer_mxfp8": (I, [P, P, P, I, P, P, P, Z, P]),
         "moe_prefetch": (I, [P, I, I, P]),
+        "moe_set_max_workgroups": (I, [I]),
         "moe_stream_read_probe": (I, [P, Z, I, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
     }
@@ -215,6 +216,11 @@ def workspace_active_experts(ws) -> int:
     import numpy as np
     off = WS_ACTIVE_EXPERTS_OFFSET
     return int(ws[off:off + 4].cpu().numpy().view(np.uint32)[0])
+
+
+def set_max_workgroups(n: int) -> None:
+    """Cap the layer kernel's grid at n workgroups (0: the default) -- moe_set_max_workgroups."""
+    _check(load().moe_set_max_workgroups(int(n)), "moe_set_max_workgroups")
 
 
 def stream_read_probe(buf, blocks_per_cu: int = 4, sink=None, stream=None):

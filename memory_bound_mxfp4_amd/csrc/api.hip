@@ -319,6 +319,12 @@ moe_status moe_workspace_status(const void* ws, size_t ws_bytes, uint32_t* statu
   return MOE_OK;
 }
 
+moe_status moe_set_max_workgroups(int n) {
+  if (n < 0) return MOE_ERR_INVALID_ARGUMENT;
+  set_layer_grid_cap(n);
+  return MOE_OK;
+}
+
 moe_status moe_stream_read_probe(const void* buf, size_t bytes, int blocks_per_cu, uint32_t* sink, void* stream) {
   if (!buf || !sink || !aligned(buf, 16) || bytes < 16 || bytes % 16 || blocks_per_cu < 1 || blocks_per_cu > 32)
     return MOE_ERR_INVALID_ARGUMENT;

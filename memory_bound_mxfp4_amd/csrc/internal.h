@@ -89,6 +89,8 @@ struct LayerArgs {
 hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* wr, int32_t* idx, hipStream_t s,
                         bool mx8 = false);
 bool mx8_supported(int H, int I);
+// Cap on the layer kernel's grid (0: two workgroups per compute unit).
+void set_layer_grid_cap(int n);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_pack_experts(uint8_t* experts, int E, int H, int I, uint8_t* scratch, bool to_packed,
                                hipStream_t s);

@@ -44,6 +44,7 @@
 // The control block at the start of the workspace is zeroed once by
 // moe_workspace_init; the last workgroup of every call resets the queue and
 // advances the call epoch (whose value + 1 is the next call's tag).
+#include <atomic>
 #include "internal.h"
 #include "moe_device.h"
 
@@ -2697,6 +2698,9 @@ static LaunchShape launch_shape(int H, int I, int E, int k, int Is, int B, bool 
   return s;
 }
 
+static std::atomic<int> g_grid_cap{0};
+void set_layer_grid_cap(int n) { g_grid_cap.store(n); }
+
 template <int RG, bool FULL, int TPL, bool MX8 = false>
 static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
   auto kern = k_moe_layer<RG, FULL, TPL, MX8>;
@@ -2709,7 +2713,8 @@ static hipError_t launch_t(LayerParams p, size_t lds, hipStream_t s) {
     cached[0] = (int)lds;
     cached[1] = per_cu;
   }
-  const int grid = num_cus() * per_cu;
+  const int cap = g_grid_cap.load();
+  const int grid = cap > 0 ? std::min(cap, num_cus() * per_cu) : num_cus() * per_cu;
   p.n_static = std::min(grid, p.n_front);
   p.nq = grid >= 16 ? 2 : 1;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, p);

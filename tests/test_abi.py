@@ -134,6 +134,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert lib.moe_workspace_status(P(0x100010), 4096, P(0x3000), None) == -1
     assert lib.moe_workspace_status(ws, 256, P(0x3000), None) == -1
     assert lib.moe_workspace_status(ws, 4096, P(0x3002), None) == -1
+    # grid cap: negative counts are rejected; 0 (the default) is accepted
+    assert lib.moe_set_max_workgroups(-1) == -1
+    assert lib.moe_set_max_workgroups(0) == 0
     # stream-read probe: NULL, size not a multiple of 16, grid shape outside 1..32 blocks per CU
     assert lib.moe_stream_read_probe(None, 1 << 20, 4, P(0x3000), None) == -1
     assert lib.moe_stream_read_probe(P(0x1000), 1000, 4, P(0x3000), None) == -1

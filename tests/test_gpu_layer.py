@@ -241,6 +241,43 @@ def test_k3_deterministic_batch64_zipf(k3_layer):
         k3_layer.router_bias = None
 
 
+@pytest.mark.parametrize("B", [1, 8, 64])
+def test_k3_small_grids_match_the_full_grid(k3_layer, B):
+    """The layer's work queue on grids of 1, 3, 16 (the smallest with two
+    queues), 17 (queues of unequal size) and 100 workgroups instead of two
+    per compute unit: each workgroup then runs long stretches of the queue,
+    in an interleaving the full grid never takes (at 1, the whole layer in
+    queue order).  Results bit-identical to the full grid's, no wait gave
+    up.  Batch 64 with the Zipf router bias (experts over several column
+    groups)."""
+    import torch
+    cfg = CONFIGS["k3_b64_zipf"] if B == 64 else CONFIGS["k3_b8" if B == 8 else "k3_b1"]
+    if B == 64:
+        k3_layer.router_bias = _dev(synth.zipf_bias(0, 0, cfg.num_experts, cfg.zipf_s))
+    try:
+        x = _dev(x_host(cfg, 0, variant=7, batch=B))
+        res0 = _dev(residual_from_x(x_host(cfg, 0, variant=7, batch=B)))
+        ws = moe.alloc_workspace(k3_layer, B)
+        r = res0.clone()
+        idx0, _ = moe.moe_decode_layer(k3_layer, x, r, ws=ws)
+        torch.cuda.synchronize()
+        ref = r.view(torch.int32).clone()
+        for grid in (1, 3, 16, 17, 100):
+            print(f"[case] layer K3 B{B} on {grid} workgroups", flush=True)
+            moe.set_max_workgroups(grid)
+            try:
+                r = res0.clone()
+                idx, _ = moe.moe_decode_layer(k3_layer, x, r, ws=ws)
+                torch.cuda.synchronize()
+            finally:
+                moe.set_max_workgroups(0)
+            assert moe.workspace_status(ws) == 0, grid
+            assert torch.equal(idx, idx0), grid
+            assert torch.equal(r.view(torch.int32), ref), grid
+    finally:
+        k3_layer.router_bias = None
+
+
 def test_workspace_reuse_and_status(k3_layer):
     """One workspace serves many calls (its control block is left cleared),
     across batch sizes it is large enough for, with no wait timing out."""
