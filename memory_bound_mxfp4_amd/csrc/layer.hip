@@ -120,6 +120,7 @@ struct LayerParams {
   int mf_cgs;    // batch > 1: shared-expert column groups (16 batch rows each)
   int n_front;   // units before the routed ones (router .. shared FC1)
   int n_static;  // units 0 .. n_static-1 go to workgroups 0 .. n_static-1
+  int n_total;   // batch 1: units in the queue (k experts); 0 for the matrix-core kernel
   int nq;        // work queues after them: 2 (1 for grids under 16 workgroups)
   int xstride;        // LDS x row stride, 16-byte granules (multiple of 8)
   int hstride;        // LDS h row stride, 16-byte granules (multiple of 8)
@@ -155,6 +156,8 @@ struct WgState {
   const int* s_row_off;
   const int* s_rows;
   const int* s_cg_off;
+  bool exited = false;     // batch 1, thread 0: this workgroup has counted itself out early
+  unsigned exit_old = 0u;  // ... and the exit count it saw
 };
 
 // Bounded poll of one control word until it has `tag` in its high half
@@ -1222,6 +1225,19 @@ __device__ __forceinline__ void post_next(const LayerParams& p, Lds& L, int it, 
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Batch 1 (thread 0): once the claimed next unit is past the end of the
+// queue, this workgroup will claim nothing more, so it counts itself out on
+// the exit counter now, during its last unit, instead of after it: the last
+// count -- and the queue reset it triggers -- then leaves the layer's end
+// one memory round trip earlier.  (The unit loop stops before claiming once
+// its index is past the end, so no claim follows a count.)
+__device__ __forceinline__ void count_out_early(const LayerParams& p, WgState& st, unsigned unext) {
+  if (p.n_total > 0 && !st.exited && queue_unit(p, unext) >= p.n_total) {
+    st.exit_old = __hip_atomic_fetch_add(p.ctrl + CTRL_EXIT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st.exited = true;
+  }
+}
+
 __device__ __forceinline__ int read_next(Lds& L, int it) {
   uint64_t v;
   while (((v = __hip_atomic_load(&L.pre, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >> 32) !=
@@ -1455,7 +1471,10 @@ __device__ __forceinline__ void fc2_unit_b1(const LayerParams& p, WgState& st, L
   };
   auto step = [&](TileBuf2& b, int pp) {
     const int q = pp + 2;
-    if (pp == post_pp) post_next(p, L, it, unext);
+    if (pp == post_pp) {
+      post_next(p, L, it, unext);
+      if (threadIdx.x == 0) count_out_early(p, st, unext);
+    }
     if (q >= P && !resolved) resolve();
     const bool own = q < P;
     const int s2 = own ? q : ((q - P) ^ (P & 1));
@@ -1525,7 +1544,7 @@ __device__ __forceinline__ int routed_fc2_run(const LayerParams& p, WgState& st,
 // sum_j gate_j * o_j in fixed j order, polling the outputs until they are
 // this call's.  Thread i owns row m = t*NT2 + i.
 template <bool OPQ>
-__device__ __forceinline__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, int t) {
+__device__ __forceinline__ void combine_unit(const LayerParams& p, WgState& st, Lds& L, int b, int t, unsigned unext) {
   const int TID_ = OPQ ? tidx() : (int)threadIdx.x;
   __syncthreads();
   const size_t s0 = (size_t)b * p.k;
@@ -1555,6 +1574,7 @@ __device__ __forceinline__ void combine_unit(const LayerParams& p, WgState& st, 
       if (q < n) acc = fmaf(L.gates[j0 + q], pair_f32(v[q]), acc);
   }
   if (!ok) set_error(p);
+  if (!OPQ && threadIdx.x == 0) count_out_early(p, st, unext);  // the claim returned before the polls did
   p.residual[(size_t)b * p.H + m] = acc;
 }
 
@@ -2570,6 +2590,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     // there recomputing per unit costs more than the set-up saves (78.5
     // against 75 us a layer).
     if constexpr (MF || !FULL) asm volatile("" : "+s"(p.H), "+s"(p.I), "+s"(p.E), "+s"(p.k), "+s"(p.Is), "+s"(p.B));
+    if (p.n_total > 0 && u >= p.n_total) break;  // batch 1: past the end, claim nothing more
     // the next unit is claimed now; its index is only needed after this one
     if (threadIdx.x == 0) nxt = claim_next(p);
     int rel = u;
@@ -2609,7 +2630,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
           if constexpr (MX8) mx_fc2_unit<FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t2);
           else mf_fc2_unit<true, FULL>(p, st, L, mfb, ae, min(gc - st.s_cg_off[ae], 3), rel % p.mf_t2);
         } else if ((rel -= NCG * p.mf_t2) < p.B * p.n_tile) {
-          combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile);
+          combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile, nxt);
         } else {
           break;
         }
@@ -2626,7 +2647,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
           u = routed_fc2_run<FULL>(p, st, L, hs, u, it, nxt);
           continue;
         } else if ((rel -= U * p.n_r2) < p.B * p.n_tile) {
-          combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile);
+          combine_unit<MF>(p, st, L, rel / p.n_tile, rel % p.n_tile, nxt);
         } else {
           break;
         }
@@ -2640,11 +2661,15 @@ __global__ __launch_bounds__(256, 2) void k_moe_layer(LayerParams p) {
     u = __builtin_amdgcn_readfirstlane(L.nxt[it & 1]);  // uniform: unit arithmetic stays scalar
     ++it;
   }
-  // Exit: the last workgroup out resets the queue and advances the epoch (all
-  // other workgroups have made their final control-block access).
+  // Exit: the last workgroup to count itself out resets the queue and
+  // advances the epoch (every other workgroup has made its final claim and
+  // read the epoch long before).  At batch 1 most count out during their
+  // last unit (count_out_early), the rest here.
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(p.ctrl + CTRL_EXIT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned old = st.exited ? st.exit_old
+                                   : __hip_atomic_fetch_add(p.ctrl + CTRL_EXIT, 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
     if (old == gridDim.x - 1) {
       st_coh(p.ctrl + CTRL_HEAD, 0u);
       st_coh(p.ctrl + CTRL_HEAD1, 0u);
@@ -2788,6 +2813,8 @@ hipError_t launch_layer(const LayerArgs& a, const float* bias, const uint16_t* w
   p.hflag = a.ws.hflag;
   p.hflag_tiles = a.ws.hflag_tiles;
   p.n_front = p.n_rt + p.n_ro + p.n_sch + p.n_s1;
+  // batch 1: the one row picks k distinct experts, so the queue's length is known here
+  p.n_total = mf ? 0 : p.n_front + a.k * p.T1 + p.n_s2 + a.k * p.n_r2 + a.B * p.n_tile;
   p.lds_h_off = sh.lds_h_off;
   p.lds_sched_off = sh.lds_sched_off;
   // top-k keys per lane in the first selection phase: E <= 1024 -> 4, else 16
