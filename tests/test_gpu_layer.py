@@ -154,11 +154,13 @@ def test_k3_batch64_zipf(k3_layer):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("B", [4, 16, 33])
+@pytest.mark.parametrize("B", [2, 4, 16, 17, 33])
 def test_k3_verify_and_ragged_batches(k3_layer, B):
-    """Verify-step batch shapes (4 and 16 rows) and a ragged one (33 rows: a
-    partial router row block and a one-row column group): every row's
-    indices, gates and outputs against the oracle."""
+    """Verify-step batch shapes (4 and 16 rows), the dispatch boundaries (2:
+    the smallest matrix-core batch; 17: the first batch whose router runs on
+    the fp64 matrix cores) and a ragged one (33 rows: a partial router row
+    block and a one-row column group): every row's indices, gates and
+    outputs against the oracle."""
     cfg = CONFIGS["k3_b8"]
     print(f"[case] layer K3 B{B} seed 0", flush=True)
     x = x_host(cfg, 0, variant=5, batch=B)
